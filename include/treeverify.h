@@ -1,0 +1,192 @@
+/*
+ * treeverify.h — C ABI of the tree-verification step of speculative decoding
+ * (one target-model pass over a whole draft tree), for AMD MI355X (gfx950).
+ *
+ * Sources, cited below by tag and section:
+ *   [P500]   "端侧多模态大模型推测解码草稿模型动态剪枝：详解基于重要性采样的树形验证并行加速策略"
+ *            https://www.ufo.work/2026/500.html
+ *   [P525]   "端侧大模型推测解码草稿模型动态剪枝策略：详解基于重要性采样的树形验证并行加速机制"
+ *            https://www.ufo.work/2026/525.html
+ *   [P537]   "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
+ *            https://www.ufo.work/2026/537.html
+ *
+ * The step has three calls, enqueued in order on one HIP stream:
+ *   tree_build_index      parent array -> depth, ancestor-or-self bitsets
+ *   tree_verify_attention every tree node attends to the shared paged prefix
+ *                         and to its own ancestors (mask M_tree)
+ *   tree_accept           ratio test, longest accepted path, residual resample
+ *
+ * Conventions shared by every call
+ *   - Every array pointer is DEVICE memory owned by the caller; the library
+ *     keeps no pointer after a call returns.  The library allocates nothing:
+ *     scratch comes from a caller-provided workspace whose size is returned
+ *     by the matching *_workspace_size query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it; no call synchronises the device or the host.
+ *     Buffers must stay alive until the stream has passed the call.
+ *   - Return value: TV_OK, or a TV_E* status when a host-side check fails (no
+ *     work is enqueued then); tree_last_error() gives the reason.
+ *   - Data-dependent faults (a bad parent index, a token outside the
+ *     vocabulary, ...) cannot be seen on the host without a sync.  Kernels OR
+ *     TV_ERR_* bits into the caller's device word `*err`, which the caller
+ *     zeroes before the first call and may read after the stream passes.
+ *     Outputs are unspecified for the sequences concerned when a bit is set.
+ *   - Trees are flattened: sequence b owns nodes cu_nodes[b] .. cu_nodes[b+1]-1
+ *     (a [batch+1] prefix-sum array).  Node indices inside a tree ("local")
+ *     run from 0; parent[i] is local, -1 meaning the node hangs directly off
+ *     the prefix ([P537] appendix B: parent index per node, -1 for the root).
+ *     Parents precede children (parent[i] < i); several nodes may hang off
+ *     the prefix.  At most TV_MAX_NODES nodes per sequence.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* host-side status codes */
+#define TV_OK 0
+#define TV_EINVAL 1          /* bad argument: null pointer, negative size, ... */
+#define TV_EUNSUPPORTED 2    /* shape or dtype the kernels do not handle */
+#define TV_EHIP 3            /* a HIP launch failed */
+#define TV_EWORKSPACE 4      /* workspace missing or smaller than required */
+
+/* device error bits OR-ed into *err */
+#define TV_ERR_BAD_PARENT 1      /* parent[i] >= i or < -1 */
+#define TV_ERR_TOO_MANY_NODES 2  /* a sequence holds more than max_nodes nodes */
+#define TV_ERR_TOKEN 4           /* drafted token outside [0, vocab) */
+#define TV_ERR_BLOCK 8           /* block id outside [0, num_blocks), or prefix longer than the
+                                    block table / max_prefix */
+#define TV_ERR_ZERO_MASS 16      /* residual and target mass both zero at the rejection node */
+#define TV_ERR_PATH 32           /* accepted path longer than max_path */
+#define TV_ERR_UNIFORM 64        /* a uniform outside [0, 1) or NaN */
+
+/* element types */
+#define TV_DTYPE_F32 0
+#define TV_DTYPE_BF16 1
+
+#define TV_MAX_NODES 2048    /* nodes per sequence (page [P525] appendix: 2048-slot KV pool) */
+#define TV_BLOCK 64          /* tokens per paged KV block ([P525] §2.3.1: 64/128-token blocks) */
+
+/*
+ * tree_build_index — per-node depth and ancestor-or-self bitset.
+ *
+ * Defines the mask of [P537] §2.2.2 (equation M_tree): node i may see node j
+ * iff j is i or an ancestor of i.  Instead of a dense N x N mask, node i gets
+ * `words` 64-bit words; bit (j % 64) of word (j / 64) is set iff j is visible
+ * to i.  depth[i] is 1 for a node under the prefix and grows by one per edge;
+ * the optional pos[i] = prefix_len[b] + depth[i] - 1 is the node's position
+ * id ([P500] §9.1, static tree position tensor).
+ *
+ *   parent      [total_nodes] int32, local parent index (-1 = under the prefix)
+ *   cu_nodes    [batch + 1] int32
+ *   max_nodes   upper bound on any sequence's node count, 1..TV_MAX_NODES
+ *   prefix_len  [batch] int32 or NULL (then pos is not written)
+ *   anc_bits    out [total_nodes, words] uint64; words >= ceil(max_nodes / 64)
+ *   depth       out [total_nodes] int32
+ *   pos         out [total_nodes] int32 or NULL
+ *   err         in/out device word, see above (TV_ERR_BAD_PARENT, TV_ERR_TOO_MANY_NODES)
+ */
+int tree_build_index(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
+                     int32_t total_nodes, int32_t max_nodes, const int32_t* prefix_len,
+                     uint64_t* anc_bits, int32_t words, int32_t* depth, int32_t* pos,
+                     int32_t* err, void* stream);
+
+/*
+ * tree_verify_attention — one attention layer over every draft-tree node.
+ *
+ * For sequence b, local node n and query head h (KV head g = h / (hq / hkv)):
+ *   visible keys = prefix positions t < prefix_len[b]  (the prefix is stored
+ *                  once and shared by every branch, [P500] §3.2; read through
+ *                  the paged block table, [P525] §2.3.1)
+ *                + tree nodes j with bit j set in anc_bits[n] ([P537] §2.2.2)
+ *   out[n, h]    = softmax_j(softmax_scale * <q[n,h], k_j[g]>) . v_j[g]
+ *   lse[n, h]    = log sum_j exp(softmax_scale * <q[n,h], k_j[g]>)   (natural log)
+ * Accumulation is fp32; bf16 probabilities feed the P.V product
+ * ([P537] appendix B; §5.1 mixed-precision accumulation).
+ *
+ *   q            [total_nodes, hq, head_dim], dtype
+ *   k_cache/v_cache [num_blocks, hkv, TV_BLOCK, head_dim], dtype: paged prefix
+ *   block_table  [batch, max_blocks] int32: physical block of logical block j
+ *                (only entries j < ceil(prefix_len[b] / 64) are read; tables
+ *                may alias the same physical blocks)
+ *   prefix_len   [batch] int32, each <= max_prefix and <= max_blocks * 64
+ *   k_tree/v_tree [total_nodes, hkv, head_dim], dtype: keys/values of the nodes
+ *   cu_nodes     [batch + 1] int32; anc_bits [total_nodes, words] from tree_build_index
+ *   max_nodes, max_prefix  host-side upper bounds that size the launch
+ *   hq % hkv == 0; head_dim 64 or 128; dtype TV_DTYPE_F32 or TV_DTYPE_BF16
+ *   out          [total_nodes, hq, head_dim], dtype
+ *   lse          [total_nodes, hq] float or NULL
+ *   workspace    device scratch of >= tree_verify_attention_workspace_size(...) bytes
+ *                (may be NULL when that size is 0)
+ *   err          TV_ERR_BLOCK, TV_ERR_TOO_MANY_NODES
+ */
+size_t tree_verify_attention_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                            int32_t max_prefix, int32_t hq, int32_t hkv,
+                                            int32_t head_dim, int32_t dtype);
+
+int tree_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                          int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* prefix_len, const void* k_tree, const void* v_tree,
+                          const int32_t* cu_nodes, const uint64_t* anc_bits, int32_t words,
+                          int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                          int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
+                          int32_t dtype, float softmax_scale, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * tree_accept — fused acceptance for every sequence, no host round-trip
+ * ([P537] §2.2.3: per-node p_accept = min(1, p_target / p_draft), one uniform
+ * per node, depth-first walk from the root cut at the first rejected node,
+ * longest accepted path, sampling fused with the traversal; [P525] §1.2:
+ * resample at the rejection point).
+ *
+ * Per sequence:
+ *   accept bit   u_accept[i] < min(1, pt_i[tok_i] / pd_i[tok_i]), evaluated
+ *                exactly as (double)u * (double)pd < (double)pt
+ *   node_ok[i]   1 iff i and all its ancestors pass
+ *   winner w     the passing node of largest depth, ties to the smallest index
+ *                (none: w = -1)
+ *   accept_len   depth(w), 0 if none; path[0 .. accept_len-1] = the root-level
+ *                ancestor of w down to w (local ids), the rest -1
+ *   rejection    c = smallest-index child of w (w = -1: smallest-index node
+ *                under the prefix); none if w has no child -> -1 outputs
+ *   resample     token drawn from norm(max(0, pt_c - pd_c)), or from pt_c when
+ *                that has no mass, by an integer inverse CDF: q_k =
+ *                floor(((double)pt - (double)pd) * 2^40) for positive
+ *                differences, Z = sum q_k, T = floor(u_resample[c] * Z)
+ *                (exact), token = smallest k with q_0 + .. + q_k > T.
+ *                Integer sums make the token independent of summation order.
+ *
+ *   p_target/p_draft [total_nodes, vocab] float: row i = the two distributions
+ *                that judged node i's drafted token (those at its parent's context)
+ *   token        [total_nodes] int32; u_accept/u_resample [total_nodes] float in [0, 1)
+ *   parent, cu_nodes as for tree_build_index; max_nodes <= TV_MAX_NODES
+ *   accept_len   out [batch] int32; path out [batch, max_path] int32
+ *   resample_node, resample_token out [batch] int32 (-1 = none)
+ *   node_ok      out [total_nodes] uint8 or NULL
+ *   workspace    >= tree_accept_workspace_size(batch, vocab) bytes
+ *   err          TV_ERR_BAD_PARENT, TV_ERR_TOO_MANY_NODES, TV_ERR_TOKEN, TV_ERR_ZERO_MASS,
+ *                TV_ERR_PATH, TV_ERR_UNIFORM
+ */
+size_t tree_accept_workspace_size(int32_t batch, int32_t vocab);
+
+int tree_accept(const float* p_target, const float* p_draft, const int32_t* token,
+                const float* u_accept, const float* u_resample, const int32_t* parent,
+                const int32_t* cu_nodes, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                int32_t vocab, int32_t max_path, int32_t* accept_len, int32_t* path,
+                int32_t* resample_node, int32_t* resample_token, uint8_t* node_ok,
+                void* workspace, size_t workspace_bytes, int32_t* err, void* stream);
+
+/* Reason for the last non-TV_OK status on the calling thread ("" if none). */
+const char* tree_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

@@ -1,0 +1,117 @@
+"""The C-ABI library: it loads, exports every entry point its header declares,
+and rejects bad arguments on the host (no GPU work is enqueued for these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verification_04_amd as tv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treeverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(tree_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tv.LIB_PATH):
+        pytest.fail("libtreeverify.so is not built (run __graft_entry__.build())")
+    return tv.load()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("tree_build_index", "tree_verify_attention", "tree_accept", "tree_last_error",
+              "tree_verify_attention_workspace_size", "tree_accept_workspace_size"):
+        assert n in names
+    assert set(names) == set(tv.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(tv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_last_error_starts_empty(lib):
+    assert lib.tree_last_error() in (b"",) or isinstance(lib.tree_last_error(), bytes)
+
+
+def test_build_index_host_checks(lib):
+    one = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    assert lib.tree_build_index(one, one, 1, 4, 0, None, one, 1, one, None, one, None) == tv.TV_EUNSUPPORTED
+    assert b"max_nodes" in lib.tree_last_error()
+    assert lib.tree_build_index(one, one, 1, 4, 3000, None, one, 47, one, None, one, None) == tv.TV_EUNSUPPORTED
+    assert lib.tree_build_index(one, one, 1, 4, 65, None, one, 1, one, None, one, None) == tv.TV_EINVAL
+    assert lib.tree_build_index(one, None, 1, 4, 64, None, one, 1, one, None, one, None) == tv.TV_EINVAL
+    assert lib.tree_build_index(one, one, -1, 4, 64, None, one, 1, one, None, one, None) == tv.TV_EINVAL
+    assert lib.tree_build_index(one, one, 1, 4, 64, None, one, 1, one, one, one, None) == tv.TV_EINVAL
+    # empty input: nothing to do, nothing launched
+    assert lib.tree_build_index(None, one, 0, 0, 64, None, None, 1, None, None, one, None) == tv.TV_OK
+
+
+def attn_call(lib, **kw):
+    one = ctypes.c_void_p(16)
+    args = dict(q=one, kc=one, vc=one, nblocks=4, bt=one, max_blocks=2, plen=one, kt=one, vt=one,
+                cu=one, anc=one, words=1, batch=1, total=3, max_nodes=3, max_prefix=100, hq=4,
+                hkv=2, d=128, dtype=tv.TV_DTYPE_BF16, scale=0.088, out=one, lse=None, ws=None,
+                ws_bytes=0, err=one, stream=None)
+    args.update(kw)
+    return lib.tree_verify_attention(*args.values())
+
+
+def test_attention_host_checks(lib):
+    assert attn_call(lib, d=96) == tv.TV_EUNSUPPORTED
+    assert attn_call(lib, dtype=7) == tv.TV_EUNSUPPORTED
+    assert attn_call(lib, hq=3) == tv.TV_EINVAL
+    assert attn_call(lib, words=0) == tv.TV_EINVAL
+    assert attn_call(lib, scale=0.0) == tv.TV_EINVAL
+    assert attn_call(lib, max_prefix=200) == tv.TV_EINVAL      # > max_blocks * 64
+    assert attn_call(lib, q=None) == tv.TV_EINVAL
+    assert attn_call(lib, err=None) == tv.TV_EINVAL
+    assert attn_call(lib, max_nodes=4096, words=64) == tv.TV_EUNSUPPORTED
+    # a short single verify splits its prefix: the workspace must be provided
+    need = lib.tree_verify_attention_workspace_size(1, 64, 64, 1088, 32, 32, 128, tv.TV_DTYPE_BF16)
+    assert need > 0
+    assert attn_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
+                     ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
+    assert b"workspace" in lib.tree_last_error()
+    # the fp32 path and wide batches need no workspace
+    assert lib.tree_verify_attention_workspace_size(1, 15, 15, 128, 4, 4, 64, tv.TV_DTYPE_F32) == 0
+    assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128, tv.TV_DTYPE_BF16) == 0
+
+
+def test_accept_host_checks(lib):
+    one = ctypes.c_void_p(16)
+    need = lib.tree_accept_workspace_size(2, 1000)
+    assert need >= 2 * 4 * 1 + 16
+
+    def call(**kw):
+        a = dict(pt=one, pd=one, tok=one, ua=one, ur=one, par=one, cu=one, batch=2, total=5,
+                 max_nodes=4, vocab=1000, max_path=4, alen=one, path=one, rn=one, rt=one,
+                 ok=None, ws=one, ws_bytes=need, err=one, stream=None)
+        a.update(kw)
+        return lib.tree_accept(*a.values())
+
+    assert call(vocab=0) == tv.TV_EUNSUPPORTED
+    assert call(vocab=1 << 19) == tv.TV_EUNSUPPORTED
+    assert call(max_nodes=5000) == tv.TV_EUNSUPPORTED
+    assert call(ws_bytes=need - 1) == tv.TV_EWORKSPACE
+    assert call(ws=None) == tv.TV_EWORKSPACE
+    assert call(pt=None) == tv.TV_EINVAL
+    assert call(path=None) == tv.TV_EINVAL
+    assert call(batch=0) == tv.TV_OK
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    par = torch.tensor([-1, 0], dtype=torch.int32)
+    cu = torch.tensor([0, 2], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tv.tree_build_index(par, cu, 2)

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer outputs (bitsets, depths, positions, accepted paths, resampled tokens,
+error words) must match bit for bit.  Attention outputs must be within
+max-abs 1e-5 (fp32 inputs) or 2e-2 (bf16 inputs, bf16 output) of the fp64
+oracle evaluated on the same input bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _helpers import (assert_accept_equal, gpu_accept, gpu_attention, gpu_index, oracle_accept,
+                      oracle_attention, rows_of, sample_nodes, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def check_index(tv, case, max_nodes=None):
+    dev = W.case_to_device(case, probs=False)
+    mn = max_nodes or max(1, case.max_nodes)
+    anc, depth, pos, err = gpu_index(tv, case, dev, mn)
+    torch.cuda.synchronize()
+    want_anc, want_depth, want_pos, want_err = oracle.build_index(case.parent, case.cu_nodes, mn,
+                                                                  case.prefix_len)
+    assert int(err.item()) == want_err
+    np.testing.assert_array_equal(anc.cpu().numpy().view(np.uint64), want_anc)
+    np.testing.assert_array_equal(depth.cpu().numpy(), want_depth)
+    np.testing.assert_array_equal(pos.cpu().numpy(), want_pos)
+    return dev, anc
+
+
+TREE_CASES = {
+    "heap15": ([W.tree_heap(15)], [128]),
+    "kary584": ([W.tree_kary_levels(8, 3)] * 2, [10, 70]),
+    "long256": ([W.tree_branch_then_chains(4, 3, 10, 256)], [0]),
+    "random_batch": ([W.tree_random(np.random.default_rng(s), n, 8) for s, n in
+                      [(1, 16), (2, 96), (3, 50), (4, 1)]], [512, 700, 4096, 3]),
+    "empty_seq": ([np.zeros(0, np.int32), W.tree_star(5), np.zeros(0, np.int32)], [64, 0, 9]),
+    "chain2048": ([W.tree_chain(2048)], [0]),
+    "star2048": ([W.tree_star(2048)], [100]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TREE_CASES))
+def test_build_index_bitexact(gpu_lib, name):
+    parents, plens = TREE_CASES[name]
+    case = W.make_case(name, parents, plens, 1, 1, 64, W.DT_F32, 10, 1, with_probs=False)
+    check_index(gpu_lib, case)
+
+
+def test_build_index_error_bits(gpu_lib):
+    bad = np.array([-1, 0, 3, 1], np.int32)   # node 2 points forward
+    case = W.make_case("bad", [bad, W.tree_heap(7)], [5, 5], 1, 1, 64, W.DT_F32, 10, 1,
+                       with_probs=False)
+    dev = W.case_to_device(case, probs=False)
+    _, _, _, err = gpu_index(gpu_lib, case, dev)
+    assert int(err.item()) == oracle.ERR_BAD_PARENT
+    # a sequence longer than max_nodes
+    case = W.make_case("big", [W.tree_chain(70)], [5], 1, 1, 64, W.DT_F32, 10, 1, with_probs=False)
+    dev = W.case_to_device(case, probs=False)
+    _, _, _, err = gpu_index(gpu_lib, case, dev, max_nodes=64)
+    assert int(err.item()) == oracle.ERR_TOO_MANY_NODES
+
+
+# ------------------------------------------------------------------ attention
+
+def check_attention(tv, case, tol, nodes=None):
+    dev, anc = check_index(tv, case)
+    out, lse, err = gpu_attention(tv, case, dev, anc)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want, want_lse = oracle_attention(case, nodes)
+    got = to_f64(out)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    if nodes is not None:
+        rows = rows_of(case, nodes)
+        got, want, got_lse, want_lse = got[rows], want[rows], got_lse[rows], want_lse[rows]
+    assert np.isfinite(got).all()
+    err_out = np.abs(got - want).max() if got.size else 0.0
+    err_lse = np.abs(got_lse - want_lse).max() if got.size else 0.0
+    assert err_out <= tol, err_out
+    assert err_lse <= tol, err_lse
+    return out
+
+
+def test_attention_tiny_fp32_config(gpu_lib):
+    check_attention(gpu_lib, W.make_config(0, with_probs=False), TOL_F32)
+
+
+SMALL = {
+    # name: (parents, prefix_lens, hq, hkv, d, dtype)
+    "ragged_bf16_gqa": ([W.tree_chain(1), W.tree_random(np.random.default_rng(5), 37, 6),
+                         W.tree_random(np.random.default_rng(6), 130, 8)], [0, 70, 200], 8, 2, 128,
+                        W.DT_BF16),
+    "wide_rows_bf16": ([W.tree_kary_levels(5, 3)], [333], 16, 4, 128, W.DT_BF16),
+    "split_prefix_mha": ([W.tree_heap(31)], [1000], 4, 4, 128, W.DT_BF16),
+    "prefix_multiple_of_64": ([W.tree_heap(7), W.tree_heap(7)], [128, 64], 8, 1, 128, W.DT_BF16),
+    "star_no_prefix": ([W.tree_star(100)], [0], 4, 2, 128, W.DT_BF16),
+    "chain_deep": ([W.tree_chain(300)], [65], 2, 1, 128, W.DT_BF16),
+    "fp32_d128": ([W.tree_random(np.random.default_rng(7), 70, 6)], [150], 4, 2, 128, W.DT_F32),
+    "bf16_d64": ([W.tree_random(np.random.default_rng(8), 70, 6)], [150], 4, 2, 64, W.DT_BF16),
+    "fp32_d64_batch": ([W.tree_heap(15), W.tree_star(3), np.zeros(0, np.int32)], [1, 64, 5], 6, 3,
+                       64, W.DT_F32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_attention_small(gpu_lib, name):
+    parents, plens, hq, hkv, d, dt = SMALL[name]
+    case = W.make_case(name, parents, plens, hq, hkv, d, dt, 10, 17, with_probs=False)
+    check_attention(gpu_lib, case, TOL_F32 if dt == W.DT_F32 else TOL_BF16)
+
+
+def test_attention_aliased_block_tables(gpu_lib):
+    parents = [W.tree_kary_levels(3, 3)] * 4
+    case = W.make_case("alias", parents, [700] * 4, 8, 2, 128, W.DT_BF16, 10, 3, alias_prefix=True,
+                       spare_blocks=5, with_probs=False)
+    check_attention(gpu_lib, case, TOL_BF16)
+
+
+def test_attention_max_node_cap(gpu_lib):
+    case = W.make_case("cap", [W.tree_random(np.random.default_rng(2), 2048, 64)], [64], 2, 1, 128,
+                       W.DT_BF16, 10, 4, with_probs=False)
+    check_attention(gpu_lib, case, TOL_BF16, nodes=sample_nodes(case, 40))
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_attention_full_configs(gpu_lib, index):
+    """The four bf16 verify workloads at full size, on sampled nodes."""
+    case = W.make_config(index, with_probs=False)
+    seqs = None if case.batch <= 8 else {0, 7, 31, 63}
+    check_attention(gpu_lib, case, TOL_BF16, nodes=sample_nodes(case, 12, seed=index, seqs=seqs))
+
+
+def test_attention_repeatable(gpu_lib):
+    case = W.make_config(1, with_probs=False)
+    dev, anc = check_index(gpu_lib, case)
+    a, la, _ = gpu_attention(gpu_lib, case, dev, anc)
+    for _ in range(5):
+        b, lb, _ = gpu_attention(gpu_lib, case, dev, anc)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ------------------------------------------------------------------ acceptance
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+def test_accept_configs_bitexact(gpu_lib, index):
+    case = W.make_config(index)
+    dev = W.case_to_device(case)
+    got = gpu_accept(gpu_lib, case, dev, 16)
+    assert_accept_equal(got, oracle_accept(case, 16))
+
+
+@pytest.mark.parametrize("index", [0, 1, 3])
+def test_accept_mostly_equal_rows(gpu_lib, index):
+    """p_target = p_draft on ~80% of nodes: long accepted paths, residuals deep in the
+    tree, and the target fallback when the rejection row has no residual mass."""
+    case = W.make_config(index)
+    rng = np.random.default_rng(index)
+    same = rng.random(case.total_nodes) < 0.8
+    case.p_target[same] = case.p_draft[same]
+    dev = W.case_to_device(case)
+    got = gpu_accept(gpu_lib, case, dev, 16)
+    want = oracle_accept(case, 16)
+    assert want["accept_len"].max() >= 2
+    assert_accept_equal(got, want)
+
+
+def test_accept_exhaustive_patterns_batched(gpu_lib):
+    """Every accept pattern of a 9-node tree, one sequence per pattern, in one call."""
+    par = W.tree_random(np.random.default_rng(3), 9, 4)
+    n, vocab = 9, 4
+    pats = 1 << n
+    parents = [par] * pats
+    case = W.make_case("pat", parents, [0] * pats, 1, 1, 64, W.DT_F32, vocab, 2, with_probs=False)
+    pt = np.full((n * pats, vocab), 0.25, np.float32)
+    for m in range(pats):
+        for i in range(n):
+            if not (m >> i) & 1:
+                pt[m * n + i] = [0.0, 0.5, 0.25, 0.25]
+    case.p_target, case.p_draft = pt, np.full_like(pt, 0.25)
+    case.token = np.zeros(n * pats, np.int32)
+    case.u_accept = np.full(n * pats, 0.5, np.float32)
+    case.u_resample = W.grid_uniforms(np.random.default_rng(1), n * pats)
+    dev = W.case_to_device(case)
+    assert_accept_equal(gpu_accept(gpu_lib, case, dev, n), oracle_accept(case, n))
+
+
+def test_accept_error_words(gpu_lib):
+    case = W.make_case("err", [W.tree_chain(3), W.tree_heap(7), W.tree_chain(4)], [0, 0, 0], 1, 1,
+                       64, W.DT_F32, 50, 9)
+    case.token[1] = 50                     # outside the vocabulary
+    case.u_accept[4] = 1.0                 # uniform outside [0, 1)
+    case.p_target[10:14] = case.p_draft[10:14]   # chain of 4 accepted, longer than max_path 3
+    dev = W.case_to_device(case)
+    got = gpu_accept(gpu_lib, case, dev, 3)
+    want = oracle_accept(case, 3)
+    assert want["err"] & oracle.ERR_TOKEN and want["err"] & oracle.ERR_UNIFORM
+    assert want["err"] & oracle.ERR_PATH
+    assert_accept_equal(got, want)
+
+
+def test_accept_zero_mass(gpu_lib):
+    case = W.make_case("zero", [W.tree_chain(2)], [0], 1, 1, 64, W.DT_F32, 8, 9)
+    case.p_target[:] = 0.0
+    dev = W.case_to_device(case)
+    got = gpu_accept(gpu_lib, case, dev, 2)
+    want = oracle_accept(case, 2)
+    assert want["err"] == oracle.ERR_ZERO_MASS
+    assert_accept_equal(got, want)
+
+
+def test_accept_bad_parent_and_cap(gpu_lib):
+    case = W.make_case("badp", [np.array([-1, 2, 0], np.int32), W.tree_heap(3)], [0, 0], 1, 1, 64,
+                       W.DT_F32, 8, 9)
+    dev = W.case_to_device(case)
+    got = gpu_accept(gpu_lib, case, dev, 4)
+    want = oracle_accept(case, 4)
+    assert want["err"] == oracle.ERR_BAD_PARENT
+    assert_accept_equal(got, want)
+
+
+def test_accept_repeatable(gpu_lib):
+    case = W.make_config(3)
+    dev = W.case_to_device(case)
+    first = gpu_accept(gpu_lib, case, dev, 16)
+    for _ in range(20):
+        again = gpu_accept(gpu_lib, case, dev, 16)
+        for k in ("accept_len", "path", "resample_node", "resample_token", "node_ok"):
+            np.testing.assert_array_equal(first[k], again[k])

@@ -1,0 +1,264 @@
+"""Python binding of libtreeverify (tree verification for speculative decoding on MI355X).
+
+Argument marshalling only: each function checks tensor devices, dtypes and
+shapes, allocates outputs with torch on the current device when the caller
+does not pass them, and calls the C entry point of the same name on torch's
+current HIP stream.  Every step of the computation runs in the HIP kernels of
+libtreeverify.so; there is no other implementation behind these functions,
+and they raise if the library is missing.
+
+Device error words: `err` is an int32 tensor of one element that the kernels
+OR TV_ERR_* bits into; functions create a zeroed one unless given one.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
+
+TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_EHIP, TV_EWORKSPACE = 0, 1, 2, 3, 4
+TV_ERR_BAD_PARENT = 1
+TV_ERR_TOO_MANY_NODES = 2
+TV_ERR_TOKEN = 4
+TV_ERR_BLOCK = 8
+TV_ERR_ZERO_MASS = 16
+TV_ERR_PATH = 32
+TV_ERR_UNIFORM = 64
+TV_DTYPE_F32, TV_DTYPE_BF16 = 0, 1
+TV_MAX_NODES = 2048
+TV_BLOCK = 64
+
+EXPORTS = (
+    "tree_build_index",
+    "tree_verify_attention_workspace_size",
+    "tree_verify_attention",
+    "tree_accept_workspace_size",
+    "tree_accept",
+    "tree_last_error",
+)
+
+_lib = None
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    P, I, Z, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.tree_build_index.argtypes = [P, P, I, I, I, P, P, I, P, P, P, P]
+    lib.tree_build_index.restype = ctypes.c_int
+    lib.tree_verify_attention_workspace_size.argtypes = [I] * 8
+    lib.tree_verify_attention_workspace_size.restype = Z
+    lib.tree_verify_attention.argtypes = [P, P, P, I, P, I, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                          I, F, P, P, P, Z, P, P]
+    lib.tree_verify_attention.restype = ctypes.c_int
+    lib.tree_accept_workspace_size.argtypes = [I, I]
+    lib.tree_accept_workspace_size.restype = Z
+    lib.tree_accept.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P, P]
+    lib.tree_accept.restype = ctypes.c_int
+    lib.tree_last_error.argtypes = []
+    lib.tree_last_error.restype = ctypes.c_char_p
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtreeverify.so (built by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is missing: build it with `python -m tree_attention_verification_04_amd.build`")
+        lib = ctypes.CDLL(path)
+        _declare(lib)
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != TV_OK:
+        raise TreeVerifyError(fn, status, load().tree_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype | tuple, dim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name} must have dtype {dts}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got {t.dim()}")
+
+
+def _err_word(err, device) -> torch.Tensor:
+    if err is None:
+        return torch.zeros(1, dtype=torch.int32, device=device)
+    _need(err, "err", torch.int32)
+    return err
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return TV_DTYPE_F32
+    if dt == torch.bfloat16:
+        return TV_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def tree_build_index(parent: torch.Tensor, cu_nodes: torch.Tensor, max_nodes: int,
+                     prefix_len: torch.Tensor | None = None, *, words: int | None = None,
+                     anc: torch.Tensor | None = None, depth: torch.Tensor | None = None,
+                     pos: torch.Tensor | None = None, err: torch.Tensor | None = None,
+                     stream=None):
+    """Depth and ancestor-or-self bitsets of flattened draft trees.
+
+    Returns (anc [total, words] int64 holding the uint64 bit patterns,
+    depth [total] int32, pos [total] int32 or None, err [1] int32).
+    """
+    lib = load()
+    _need(parent, "parent", torch.int32, 1)
+    _need(cu_nodes, "cu_nodes", torch.int32, 1)
+    dev = parent.device
+    total = parent.numel()
+    batch = cu_nodes.numel() - 1
+    words = words if words is not None else max(1, math.ceil(max_nodes / 64))
+    if anc is None:
+        anc = torch.empty((total, words), dtype=torch.int64, device=dev)
+    if depth is None:
+        depth = torch.empty(total, dtype=torch.int32, device=dev)
+    if prefix_len is not None:
+        _need(prefix_len, "prefix_len", torch.int32, 1)
+        if pos is None:
+            pos = torch.empty(total, dtype=torch.int32, device=dev)
+    err = _err_word(err, dev)
+    _check("tree_build_index",
+           lib.tree_build_index(_ptr(parent), _ptr(cu_nodes), batch, total, max_nodes,
+                                _ptr(prefix_len), _ptr(anc), words, _ptr(depth),
+                                _ptr(pos) if prefix_len is not None else None, _ptr(err),
+                                _stream(stream)))
+    return anc, depth, (pos if prefix_len is not None else None), err
+
+
+def tree_verify_attention_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq, hkv,
+                                         head_dim, dtype: int) -> int:
+    return int(load().tree_verify_attention_workspace_size(batch, total_nodes, max_nodes,
+                                                           max_prefix, hq, hkv, head_dim, dtype))
+
+
+def tree_verify_attention(q, k_cache, v_cache, block_table, prefix_len, k_tree, v_tree, cu_nodes,
+                          anc, max_nodes: int, max_prefix: int, scale: float | None = None, *,
+                          out=None, lse=None, want_lse: bool = True, workspace=None, err=None,
+                          stream=None):
+    """Tree attention over the paged prefix and each node's ancestors.
+
+    q [total, hq, D]; k_cache/v_cache [num_blocks, hkv, 64, D]; block_table
+    [batch, max_blocks] int32; prefix_len [batch] int32; k_tree/v_tree
+    [total, hkv, D]; anc from tree_build_index.  Returns (out, lse, err).
+    """
+    lib = load()
+    fdt = (torch.float32, torch.bfloat16)
+    _need(q, "q", fdt, 3)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype, 4)
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        _need(t, name, q.dtype, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_len, "prefix_len", torch.int32, 1)
+    _need(cu_nodes, "cu_nodes", torch.int32, 1)
+    _need(anc, "anc", torch.int64, 2)
+    total, hq, d = q.shape
+    num_blocks, hkv, blk, d2 = k_cache.shape
+    if blk != TV_BLOCK or d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks, hkv, 64, head_dim]")
+    if tuple(k_tree.shape) != (total, hkv, d) or tuple(v_tree.shape) != (total, hkv, d):
+        raise ValueError("k_tree/v_tree must be [total_nodes, hkv, head_dim]")
+    if anc.shape[0] != total:
+        raise ValueError("anc must have one row per node")
+    batch = cu_nodes.numel() - 1
+    if block_table.shape[0] != batch or prefix_len.numel() != batch:
+        raise ValueError("block_table / prefix_len must have one row per sequence")
+    dt = dtype_code(q.dtype)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((total, hq), dtype=torch.float32, device=q.device)
+    need = tree_verify_attention_workspace_size(batch, total, max_nodes, max_prefix, hq, hkv, d, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, q.device)
+    _check("tree_verify_attention",
+           lib.tree_verify_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), num_blocks,
+                                     _ptr(block_table), block_table.shape[1], _ptr(prefix_len),
+                                     _ptr(k_tree), _ptr(v_tree), _ptr(cu_nodes), _ptr(anc),
+                                     anc.shape[1], batch, total, max_nodes, max_prefix, hq, hkv,
+                                     d, dt, scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                                     ws_bytes, _ptr(err), _stream(stream)))
+    return out, lse, err
+
+
+def tree_accept_workspace_size(batch: int, vocab: int) -> int:
+    return int(load().tree_accept_workspace_size(batch, vocab))
+
+
+def tree_accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes: int,
+                max_path: int, *, node_ok=True, outputs: dict | None = None, workspace=None,
+                err=None, stream=None) -> dict:
+    """Ratio test, longest accepted path and residual resample for every sequence.
+
+    Returns dict(accept_len [B], path [B, max_path], resample_node [B],
+    resample_token [B], node_ok [total] uint8 or None, err [1]).
+    """
+    lib = load()
+    _need(p_target, "p_target", torch.float32, 2)
+    _need(p_draft, "p_draft", torch.float32, 2)
+    for name, t in (("token", token), ("parent", parent), ("cu_nodes", cu_nodes)):
+        _need(t, name, torch.int32, 1)
+    for name, t in (("u_accept", u_accept), ("u_resample", u_resample)):
+        _need(t, name, torch.float32, 1)
+    total, vocab = p_target.shape
+    if tuple(p_draft.shape) != (total, vocab):
+        raise ValueError("p_draft must match p_target")
+    batch = cu_nodes.numel() - 1
+    dev = p_target.device
+    o = outputs if outputs is not None else {}
+    if not o:
+        o["accept_len"] = torch.empty(batch, dtype=torch.int32, device=dev)
+        o["path"] = torch.empty((batch, max_path), dtype=torch.int32, device=dev)
+        o["resample_node"] = torch.empty(batch, dtype=torch.int32, device=dev)
+        o["resample_token"] = torch.empty(batch, dtype=torch.int32, device=dev)
+        o["node_ok"] = torch.empty(total, dtype=torch.uint8, device=dev) if node_ok else None
+    need = tree_accept_workspace_size(batch, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    err = _err_word(err, dev)
+    o["err"] = err
+    _check("tree_accept",
+           lib.tree_accept(_ptr(p_target), _ptr(p_draft), _ptr(token), _ptr(u_accept),
+                           _ptr(u_resample), _ptr(parent), _ptr(cu_nodes), batch, total,
+                           max_nodes, vocab, max_path, _ptr(o["accept_len"]), _ptr(o["path"]),
+                           _ptr(o["resample_node"]), _ptr(o["resample_token"]),
+                           _ptr(o.get("node_ok")), _ptr(workspace),
+                           workspace.numel(), _ptr(err), _stream(stream)))
+    return o

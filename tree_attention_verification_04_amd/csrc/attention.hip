@@ -1,0 +1,176 @@
+// tree_verify_attention: argument checks, launch plan, split-KV combine.
+//
+// The plan picks the kernel (matrix-core for bf16 head_dim 128, vector ALU
+// otherwise) and, for the matrix-core kernel, how many workgroups share one
+// (sequence, KV head) prefix.  When one row tile per KV head cannot fill the
+// 256 compute units (a single short verify), the prefix blocks are split over
+// several workgroups and their partial results merged by log-sum-exp:
+//   lse = log sum_i exp(lse_i),  out = sum_i exp(lse_i - lse) * out_i,
+// the same rescaling the online softmax applies between tiles (page
+// "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
+// (ufo.work/2026/537), appendix B).
+#include <algorithm>
+
+#include "attn.h"
+
+namespace tv {
+
+AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
+                        int head_dim, int dtype) {
+  AttnPlan p{};
+  p.mfma = dtype == TV_DTYPE_BF16 && head_dim == 128;
+  p.splits = 1;
+  p.blocks_per_split = 0;
+  p.row_tiles = 0;
+  p.total_work = 0;
+  p.workspace = 0;
+  if (!p.mfma || batch <= 0 || hkv <= 0) return p;
+  const int group = hq / hkv;
+  const int nblk = ceil_div(std::max(0, max_prefix), 64);
+  p.row_tiles = std::max(1, ceil_div(group * max_nodes, kMfmaRowsPerWG));
+  const long base = static_cast<long>(batch) * hkv * p.row_tiles;
+  if (nblk > 1 && base < 2 * kCUs) {
+    const int want = std::min(nblk, ceil_div(2 * kCUs, static_cast<int>(base)));
+    p.blocks_per_split = ceil_div(nblk, want);
+    p.splits = ceil_div(nblk, p.blocks_per_split);
+  } else {
+    p.blocks_per_split = std::max(1, nblk);
+    p.splits = 1;
+  }
+  p.total_work = base * p.splits;
+  if (p.splits > 1) {
+    const size_t rows = static_cast<size_t>(total_nodes) * hq;
+    const size_t o_bytes = static_cast<size_t>(p.splits) * rows * head_dim * sizeof(float);
+    const size_t l_bytes = static_cast<size_t>(p.splits) * rows * sizeof(float);
+    p.workspace = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
+  }
+  return p;
+}
+
+// One wavefront per (node, head) row merges the split partials.
+__global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long row = static_cast<long>(blockIdx.x) * 4 + wave;
+  if (row >= a.total_rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_lse[s * static_cast<long>(a.total_rows) + row]);
+  float w_sum = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < a.splits; ++s) {
+      const float ls = a.part_lse[s * static_cast<long>(a.total_rows) + row];
+      const float w = expf(ls - mx);
+      const float2 o = *reinterpret_cast<const float2*>(
+          a.part_o + (s * static_cast<long>(a.total_rows) + row) * 128 + 2 * lane);
+      w_sum += w;
+      o0 = fmaf(w, o.x, o0);
+      o1 = fmaf(w, o.y, o1);
+    }
+  }
+  const float inv = w_sum > 0.0f ? 1.0f / w_sum : 0.0f;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + row * 128 + 2 * lane;
+  out[0] = f32_to_bf16(o0 * inv);
+  out[1] = f32_to_bf16(o1 * inv);
+  if (a.lse != nullptr && lane == 0) a.lse[row] = w_sum > 0.0f ? mx + logf(w_sum) : -INFINITY;
+}
+
+int launch_attn_combine(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_attn_combine, dim3(ceil_div(a.total_rows, 4)), dim3(256), 0, s, a);
+  return check_launch("tree_verify_attention/combine");
+}
+
+}  // namespace tv
+
+extern "C" size_t tree_verify_attention_workspace_size(int32_t batch, int32_t total_nodes,
+                                                       int32_t max_nodes, int32_t max_prefix,
+                                                       int32_t hq, int32_t hkv, int32_t head_dim,
+                                                       int32_t dtype) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return 0;
+  return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype)
+      .workspace;
+}
+
+extern "C" int tree_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                                     int32_t num_blocks, const int32_t* block_table,
+                                     int32_t max_blocks, const int32_t* prefix_len,
+                                     const void* k_tree, const void* v_tree,
+                                     const int32_t* cu_nodes, const uint64_t* anc_bits,
+                                     int32_t words, int32_t batch, int32_t total_nodes,
+                                     int32_t max_nodes, int32_t max_prefix, int32_t hq,
+                                     int32_t hkv, int32_t head_dim, int32_t dtype,
+                                     float softmax_scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, int32_t* err, void* stream) {
+  tv::clear_error();
+  if (batch < 0 || total_nodes < 0 || max_prefix < 0 || num_blocks < 0 || max_blocks < 0)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: negative size");
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: hq must be a positive multiple of hkv");
+  if (head_dim != 64 && head_dim != 128)
+    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: head_dim must be 64 or 128");
+  if (dtype != TV_DTYPE_F32 && dtype != TV_DTYPE_BF16)
+    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: dtype must be F32 or BF16");
+  if (max_nodes < 1 || max_nodes > TV_MAX_NODES)
+    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: max_nodes must be in [1, 2048]");
+  if (words < tv::ceil_div(max_nodes, 64))
+    return tv::fail(TV_EINVAL, "tree_verify_attention: words < ceil(max_nodes / 64)");
+  if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: softmax_scale must be positive and finite");
+  if (err == nullptr || cu_nodes == nullptr)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: null err or cu_nodes");
+  if (batch == 0 || total_nodes == 0) return TV_OK;
+  if (q == nullptr || k_tree == nullptr || v_tree == nullptr || anc_bits == nullptr ||
+      out == nullptr || prefix_len == nullptr)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: null q, tree K/V, anc_bits, out or prefix_len");
+  if (max_prefix > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
+    return tv::fail(TV_EINVAL, "tree_verify_attention: null paged cache or block table");
+  if (static_cast<long>(max_blocks) * 64 < max_prefix)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: max_prefix exceeds max_blocks * 64");
+  if (static_cast<long>(total_nodes) * hq > INT32_MAX)
+    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: too many (node, head) rows");
+
+  const tv::AttnPlan plan =
+      tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+    return tv::fail(TV_EWORKSPACE, "tree_verify_attention: workspace missing or too small");
+
+  tv::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.prefix_len = prefix_len;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.cu_nodes = cu_nodes;
+  a.anc = anc_bits;
+  a.out = out;
+  a.lse = lse;
+  a.err = err;
+  a.words = words;
+  a.batch = batch;
+  a.total_nodes = total_nodes;
+  a.total_rows = total_nodes * hq;
+  a.max_nodes = max_nodes;
+  a.max_prefix = max_prefix;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.group = hq / hkv;
+  a.scale = softmax_scale;
+  a.splits = plan.splits;
+  a.blocks_per_split = plan.blocks_per_split;
+  a.row_tiles = plan.row_tiles;
+  a.total_work = static_cast<int>(plan.total_work);
+  if (plan.splits > 1) {
+    const size_t rows = static_cast<size_t>(total_nodes) * hq;
+    const size_t o_bytes = static_cast<size_t>(plan.splits) * rows * head_dim * sizeof(float);
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          ((o_bytes + 255) & ~static_cast<size_t>(255)));
+  }
+  auto s = static_cast<hipStream_t>(stream);
+  if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
+  int st = tv::launch_attn_mfma(a, s);
+  if (st != TV_OK || plan.splits == 1) return st;
+  return tv::launch_attn_combine(a, s);
+}

@@ -1,0 +1,50 @@
+// Internal interface between the tree-attention entry point and its kernels.
+#pragma once
+
+#include "tv_common.h"
+
+namespace tv {
+
+// Everything a tree-attention kernel reads, by value.
+struct AttnArgs {
+  const void* q;            // [total_nodes, hq, D]
+  const void* k_cache;      // [num_blocks, hkv, 64, D]
+  const void* v_cache;
+  const int32_t* block_table;  // [batch, max_blocks]
+  const int32_t* prefix_len;   // [batch]
+  const void* k_tree;       // [total_nodes, hkv, D]
+  const void* v_tree;
+  const int32_t* cu_nodes;  // [batch + 1]
+  const uint64_t* anc;      // [total_nodes, words]
+  void* out;                // [total_nodes, hq, D]
+  float* lse;               // [total_nodes, hq] or null
+  float* part_o;            // [splits, total_rows, D] fp32 (split-KV partials)
+  float* part_lse;          // [splits, total_rows]
+  int32_t* err;
+  int words, batch, total_nodes, total_rows, max_nodes, max_prefix;
+  int num_blocks, max_blocks, hq, hkv, group;
+  int splits, blocks_per_split, row_tiles, total_work;
+  float scale;              // softmax scale (natural-exp units)
+};
+
+// How one launch is laid out; the same function sizes the workspace.
+struct AttnPlan {
+  bool mfma;          // bf16, head_dim 128: matrix-core kernel; else the vector kernel
+  int splits;         // prefix split across workgroups (1 = no combine pass)
+  int blocks_per_split;
+  int row_tiles;      // row tiles per (sequence, kv head)
+  long total_work;    // workgroups with work
+  size_t workspace;   // bytes of split partials
+};
+
+AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
+                        int head_dim, int dtype);
+
+int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
+int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+int launch_attn_combine(const AttnArgs& a, hipStream_t s);
+
+constexpr int kMfmaRowsPerWG = 128;  // 4 waves x 32 rows
+constexpr int kCUs = 256;
+
+}  // namespace tv

@@ -1,0 +1,375 @@
+// Matrix-core tree attention for gfx950: bf16 Q/K/V, head_dim 128, fp32 accumulation.
+//
+// Work unit: (sequence b, KV head g, row tile, prefix split).  The rows of one KV
+// head are the G * N_b pairs (node, query head of the group), ordered node-major;
+// a workgroup of 4 wavefronts takes 128 of them, 32 per wavefront.  It streams the
+// prefix of sequence b through the block table, one 64-token paged block at a
+// time, and then the 64-node tiles of the tree that any of its rows can see.  Each
+// tile is staged once in LDS and used by all 128 rows: the shared prefix is read
+// once per tile for every node of the tree (page "端侧多模态大模型推测解码草稿模型动态剪枝：
+// 详解基于重要性采样的树形验证并行加速策略" (ufo.work/2026/500), §3.2: common prefix kept
+// once and reused; all branches flattened into one launch).
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: a lane
+// then holds 16 keys of a single row per 32-key sub-tile, so the row max and sum
+// need one cross-lane exchange (lane ^ 32) instead of a shuffle tree.  The K rows
+// fed to the MFMA are permuted (4-row groups 1<->2 and 5<->6 of every 32) so that
+// the accumulator registers of a lane hold 8 consecutive keys per 16-key step; the
+// probabilities are then packed to bf16 and used directly as the B operand of
+// O^T = V^T P^T, with V stored transposed in LDS so each A operand is one 16-byte
+// read.  Online softmax with running max and sum in fp32 (page
+// "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
+// (ufo.work/2026/537), appendix B: running max m, sum l, rescale by exp(m_old - m_new),
+// bf16 probabilities into the P.V product); the tree mask M_tree (same page, §2.2.2)
+// comes from the 64-bit ancestor word of the row's node for the tile.
+//
+// Tiles are double-buffered: the next tile's global loads are issued into
+// registers before the current tile's matrix work, and written to the other LDS
+// buffer after it; one barrier per tile.  Work indices are remapped so that the
+// workgroups sharing a (sequence, KV head, split) land on the same XCD and hit
+// its L2 for the shared K/V tiles.
+#include "attn.h"
+
+namespace tv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 128;
+constexpr int kKT = 64;                       // keys per tile
+constexpr int kKStride = kD + 8;              // bf16 per K row in LDS (272 B)
+constexpr int kVStride = kKT + 8;             // bf16 per V^T row in LDS (144 B)
+constexpr int kKBytes = kKT * kKStride * 2;   // 17408
+constexpr int kVBytes = kD * kVStride * 2;    // 18432
+constexpr int kBufBytes = kKBytes + kVBytes;  // 35840
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// MFMA row m of a 32-key sub-tile reads key perm(m): swaps 4-row groups 1<->2, 5<->6.
+__device__ __forceinline__ int key_perm(int m) {
+  const int grp = m >> 2;
+  const int swapped = (grp & 3) == 1 ? grp + 1 : ((grp & 3) == 2 ? grp - 1 : grp);
+  return (swapped << 2) | (m & 3);
+}
+
+struct TileSrc {
+  const uint16_t* k;  // first row of the tile (row stride kRowStride elements)
+  const uint16_t* v;
+  long row_stride;    // elements between consecutive keys
+  int nvalid;         // rows [0, nvalid) exist; later rows are zero-filled
+};
+
+// Global -> registers for one tile: 4 K chunks and 4x(4 keys) V chunks per thread.
+struct TileRegs {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+__device__ __forceinline__ void load_tile(const TileSrc& src, int tid, TileRegs& r) {
+  const int dc = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = (tid >> 4) + 16 * i;
+    r.k[i] = key < src.nvalid
+                 ? *reinterpret_cast<const uint4*>(src.k + key * src.row_stride + dc * 8)
+                 : make_uint4(0, 0, 0, 0);
+  }
+  const int kq = tid >> 4;  // keys 4kq .. 4kq+3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = 4 * kq + i;
+    r.v[i] = key < src.nvalid
+                 ? *reinterpret_cast<const uint4*>(src.v + key * src.row_stride + dc * 8)
+                 : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_tile(char* buf, int tid, const TileRegs& r) {
+  const int dc = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = (tid >> 4) + 16 * i;
+    *reinterpret_cast<uint4*>(buf + key * (kKStride * 2) + dc * 16) = r.k[i];
+  }
+  // V^T[d][key]: for each of the 8 d of this chunk, the 4 keys 4kq..4kq+3
+  char* vt = buf + kKBytes;
+  const int kq = tid >> 4;
+  const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+  const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+  const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
+  const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // d = 8dc + 2j (low halves) and 8dc + 2j + 1 (high halves)
+    const uint2 lo = make_uint2((w0[j] & 0xffffu) | (w1[j] << 16), (w2[j] & 0xffffu) | (w3[j] << 16));
+    const uint2 hi = make_uint2((w0[j] >> 16) | (w1[j] & 0xffff0000u),
+                                (w2[j] >> 16) | (w3[j] & 0xffff0000u));
+    const int d = 8 * dc + 2 * j;
+    *reinterpret_cast<uint2*>(vt + d * (kVStride * 2) + kq * 8) = lo;
+    *reinterpret_cast<uint2*>(vt + (d + 1) * (kVStride * 2) + kq * 8) = hi;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ uint32_t s_tree_mask;
+
+  // ---- work item (XCD-aware: consecutive work indices share an XCD)
+  const int per_xcd = gridDim.x / 8;
+  const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (work >= a.total_work) return;
+  const int tile = work % a.row_tiles;
+  const int rest = work / a.row_tiles;
+  const int split = rest % a.splits;
+  const int pair = rest / a.splits;
+  const int g = pair % a.hkv;
+  const int b = pair / a.hkv;
+
+  const int n0 = a.cu_nodes[b];
+  int count = a.cu_nodes[b + 1] - n0;
+  int plen = a.prefix_len[b];
+  const int tid = threadIdx.x;
+  if (count > a.max_nodes) {
+    if (tid == 0 && tile == 0 && split == 0) atomicOr(a.err, TV_ERR_TOO_MANY_NODES);
+    count = a.max_nodes;
+  }
+  if (plen < 0 || plen > a.max_prefix || plen > a.max_blocks * 64) {
+    if (tid == 0 && tile == 0 && split == 0) atomicOr(a.err, TV_ERR_BLOCK);
+    plen = max(0, min(plen, min(a.max_prefix, a.max_blocks * 64)));
+  }
+  const int rows = a.group * count;
+  const int r0 = tile * kMfmaRowsPerWG;
+  if (r0 >= rows) return;
+
+  const int nblk = (plen + kKT - 1) / kKT;
+  const int kb0 = split * a.blocks_per_split;
+  const int kb1 = min(nblk, kb0 + a.blocks_per_split);
+  const int n_prefix_tiles = max(0, kb1 - kb0);
+  const bool do_tree = split == a.splits - 1;
+
+  // ---- which 64-node tree tiles any row of this workgroup can see
+  if (tid == 0) s_tree_mask = 0;
+  __syncthreads();
+  const int ntw = (count + 63) / 64;
+  if (do_tree) {
+    const int lo = r0 / a.group;
+    const int hi = (min(rows, r0 + kMfmaRowsPerWG) - 1) / a.group;
+    const int pairs_n = (hi - lo + 1) * ntw;
+    uint32_t m = 0;
+    for (int i = tid; i < pairs_n; i += kThreads) {
+      const int nd = lo + i / ntw, t = i % ntw;
+      if (a.anc[static_cast<long>(n0 + nd) * a.words + t] != 0) m |= 1u << t;
+    }
+    if (m) atomicOr(&s_tree_mask, m);
+  }
+  __syncthreads();
+  const uint32_t tree_mask = do_tree ? s_tree_mask : 0u;
+  const int n_tiles = n_prefix_tiles + __popc(tree_mask);
+
+  // ---- this lane's row and its Q fragment (B operand of S^T = K Q^T)
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+  const int r = r0 + wave * 32 + col;
+  const bool row_ok = r < rows;
+  const int node = row_ok ? r / a.group : 0;
+  const int head = g * a.group + (row_ok ? r % a.group : 0);
+  const long grow = static_cast<long>(n0 + node) * a.hq + head;  // global row (node, head)
+  const bool wave_live = r0 + wave * 32 < rows;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + grow * kD + half * 8;
+  bf16x8_t qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qf[s] = as_bf16x8(row_ok ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0));
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const uint16_t* kt = static_cast<const uint16_t*>(a.k_tree);
+  const uint16_t* vt = static_cast<const uint16_t*>(a.v_tree);
+
+  // tile it -> source rows, and (for masking) its kind and base index
+  auto tile_src = [&](int it, int& kind, int& base) -> TileSrc {
+    TileSrc s;
+    if (it < n_prefix_tiles) {
+      const int kb = kb0 + it;
+      int blk = a.block_table[static_cast<long>(b) * a.max_blocks + kb];
+      kind = 0;
+      base = kb * kKT;
+      if (blk < 0 || blk >= a.num_blocks) {
+        if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
+        s.k = kc;
+        s.v = vc;
+        s.row_stride = kD;
+        s.nvalid = 0;
+        return s;
+      }
+      const long off = (static_cast<long>(blk) * a.hkv + g) * kKT * kD;
+      s.k = kc + off;
+      s.v = vc + off;
+      s.row_stride = kD;
+      s.nvalid = min(kKT, plen - base);
+    } else {
+      uint32_t m = tree_mask;
+      for (int j = it - n_prefix_tiles; j > 0; --j) m &= m - 1;
+      const int t = __ffs(m) - 1;
+      kind = 1;
+      base = t;
+      const long off = (static_cast<long>(n0 + t * 64) * a.hkv + g) * kD;
+      s.k = kt + off;
+      s.v = vt + off;
+      s.row_stride = static_cast<long>(a.hkv) * kD;
+      s.nvalid = min(64, count - t * 64);
+    }
+    return s;
+  };
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float c2 = a.scale * kLog2e;
+  const int krow0 = key_perm(col);
+  const uint64_t* anc_row = a.anc + static_cast<long>(n0 + node) * a.words;
+
+  TileRegs regs;
+  int kind_cur = 0, base_cur = 0;
+  if (n_tiles > 0) {
+    TileSrc s0 = tile_src(0, kind_cur, base_cur);
+    load_tile(s0, tid, regs);
+    store_tile(smem, tid, regs);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_tiles; ++it) {
+    char* buf = smem + (it & 1) * kBufBytes;
+    int kind_nxt = 0, base_nxt = 0;
+    const bool more = it + 1 < n_tiles;
+    if (more) {
+      TileSrc sn = tile_src(it + 1, kind_nxt, base_nxt);
+      load_tile(sn, tid, regs);
+    }
+    if (wave_live) {
+      // S^T for two 32-key sub-tiles
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        sacc[sg] = f32x16_t{};
+        const char* kr = buf + (32 * sg + krow0) * (kKStride * 2) + half * 16;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(kr + s * 32));
+          sacc[sg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sg], 0, 0, 0);
+        }
+      }
+      // mask: key index of register v of sub-tile sg is 32sg + 16(v/8) + 8*half + v%8
+      uint64_t vis;
+      if (kind_cur == 0) {
+        const int nv = plen - base_cur;  // keys [0, nv) of this block are in the prefix
+        vis = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+      } else {
+        vis = row_ok ? anc_row[base_cur] : 0ull;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kk = 32 * sg + 16 * (v >> 3) + 8 * half + (v & 7);
+          const float sv = ((vis >> kk) & 1ull) ? sacc[sg][v] : -INFINITY;
+          sacc[sg][v] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+      const float mc = m_use * c2;
+      float psum = 0.0f;
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[sg][v] * c2 - mc);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[sg][v + 1] * c2 - mc);
+          psum += p0 + p1;
+          pk[sg][v >> 1] = pack2_bf16(p0, p1);
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] *= alpha;
+      // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sg = j >> 1, vb = (j & 1) * 4;
+        const uint4 pw = make_uint4(pk[sg][vb], pk[sg][vb + 1], pk[sg][vb + 2], pk[sg][vb + 3]);
+        const bf16x8_t pf = as_bf16x8(pw);
+        const char* vr = buf + kKBytes + col * (kVStride * 2) + (16 * j + 8 * half) * 2;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const uint4*>(vr + dt * 32 * (kVStride * 2)));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) store_tile(smem + ((it + 1) & 1) * kBufBytes, tid, regs);
+    kind_cur = kind_nxt;
+    base_cur = base_nxt;
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse = l_tot > 0.0f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+  // register v of d-tile dt holds d = 32dt + 8(v/4) + 4*half + v%4
+  if (a.splits == 1) {
+    uint16_t* out = static_cast<uint16_t*>(a.out) + grow * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d = 32 * dt + 8 * qd + 4 * half;
+        const uint2 w = make_uint2(pack2_bf16(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv),
+                                   pack2_bf16(acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv));
+        *reinterpret_cast<uint2*>(out + d) = w;
+      }
+    if (a.lse != nullptr && half == 0) a.lse[grow] = lse;
+  } else {
+    float* po = a.part_o + (static_cast<long>(split) * a.total_rows + grow) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d = 32 * dt + 8 * qd + 4 * half;
+        *reinterpret_cast<float4*>(po + d) =
+            make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv,
+                        acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv);
+      }
+    if (half == 0) a.part_lse[static_cast<long>(split) * a.total_rows + grow] = lse;
+  }
+}
+
+int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBufBytes);
+    attr_set = true;
+  }
+  const int grid = 8 * ceil_div(a.total_work, 8);
+  hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(kThreads), 2 * kBufBytes, s, a);
+  return check_launch("tree_verify_attention/mfma");
+}
+
+}  // namespace tv

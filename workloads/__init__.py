@@ -412,3 +412,34 @@ def make_config(index: int, seed: int = 1234, with_probs: bool = True) -> Case:
     parents, plens, hq, hkv, d, dt, vocab, alias = config_trees(index, seed)
     return make_case(CONFIG_NAMES[index], parents, plens, hq, hkv, d, dt, vocab, seed,
                      alias_prefix=alias, with_probs=with_probs)
+
+
+# --------------------------------------------------------------------------
+# device upload (torch); the same bytes as the numpy arrays above
+# --------------------------------------------------------------------------
+def to_torch(a: np.ndarray, dtype: int | None = None, device="cuda"):
+    """numpy -> torch tensor on `device`; bf16 bit arrays become torch.bfloat16."""
+    import torch
+    if dtype == DT_BF16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def case_to_device(case: Case, device="cuda", probs: bool = True) -> dict:
+    """Every input of a Case as device tensors, keyed by argument name."""
+    dt = case.dtype
+    out = dict(
+        q=to_torch(case.q, dt, device), k_cache=to_torch(case.k_cache, dt, device),
+        v_cache=to_torch(case.v_cache, dt, device), k_tree=to_torch(case.k_tree, dt, device),
+        v_tree=to_torch(case.v_tree, dt, device), block_table=to_torch(case.block_table, None, device),
+        prefix_len=to_torch(case.prefix_len, None, device), cu_nodes=to_torch(case.cu_nodes, None, device),
+        parent=to_torch(case.parent, None, device))
+    if probs and case.p_target is not None:
+        out.update(p_target=to_torch(case.p_target, None, device),
+                   p_draft=to_torch(case.p_draft, None, device),
+                   token=to_torch(case.token, None, device),
+                   u_accept=to_torch(case.u_accept, None, device),
+                   u_resample=to_torch(case.u_resample, None, device))
+    return out
