@@ -1,0 +1,249 @@
+"""Verify-step benchmark on one MI355X.
+
+One step = one pass of the whole verify path over one batch of synthetic,
+HBM-resident input: tree_build_index + tree_verify_attention (one attention
+layer) + tree_accept.  The step is captured once in a HIP graph and replayed
+(launch overhead is what graph capture removes from a verify step); the eager
+rate is reported beside it.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+
+--config selects the workload (0..4, default 1: LLaVA-7B-like single verify,
+batch 1, prefix 1088, 64-node importance-sampled tree, 32 heads MHA,
+head_dim 128, bf16, vocab 32000).
+
+`roofline` is for the attention call (the dominant kernel): algorithmic bytes
+(unique prefix K+V, tree K+V, Q, out) or flops (4*D*Hq*sum over nodes of the
+visible keys) per launch divided by its average duration, timed with events on
+the launch stream over back-to-back graph-replayed launches.  `cpu_baseline`
+is the CPU oracle (fp64 numpy + Python) timed on this host on a bounded
+number of whole steps of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix
+VALU_FP32_PEAK_TFS = 157.3     # MI355X fp32 vector
+
+
+def attention_cost(case):
+    """Algorithmic bytes and flops of one tree-attention launch."""
+    import oracle
+    esz = 2 if case.dtype == 1 else 4
+    d, hq, hkv = case.d, case.hq, case.hkv
+    total = case.total_nodes
+    prefix_tokens = int(case.prefix_len.sum())
+    if case.batch > 1 and np.all(case.block_table == case.block_table[:1]):
+        prefix_tokens = int(case.prefix_len.max())  # one physical prefix read through every table
+    bytes_ = (prefix_tokens * hkv * d * 2 + total * hkv * d * 2 + 2 * total * hq * d) * esz
+    visible = 0
+    for b in range(case.batch):
+        dep = oracle.depths(case.local_parent(b))
+        visible += int(case.prefix_len[b]) * len(dep) + int(dep.sum())
+    flops = 4.0 * d * hq * visible
+    return bytes_, flops
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(case, budget_s: float = 10.0):
+    """The oracle, as it stands, on whole steps of the workload until ~budget_s."""
+    import oracle
+    import workloads as W
+    f = lambda a: W.to_f64(a, case.dtype)
+    args = (f(case.q), f(case.k_cache), f(case.v_cache))
+    kt, vt = f(case.k_tree), f(case.v_tree)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.build_index(case.parent, case.cu_nodes, max(1, case.max_nodes), case.prefix_len)
+        oracle.tree_attention(*args, case.block_table, case.prefix_len, kt, vt, case.cu_nodes,
+                              case.parent, case.hq, case.hkv, case.scale)
+        oracle.accept(case.p_target, case.p_draft, case.token, case.u_accept, case.u_resample,
+                      case.parent, case.cu_nodes, case.vocab, 16)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 1000:
+            break
+    return dict(value=case.total_nodes * steps / el, unit="tokens/s", cores=blas_threads(),
+                kind="oracle",
+                sample=f"{steps} whole verify steps of the same workload (index + attention + "
+                       f"acceptance) in {el:.1f} s; fp64 numpy BLAS + Python loops")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import tree_attention_verification_04_amd as tv
+    import workloads as W
+
+    tv.load()
+    torch.cuda.set_device(0)
+    case = W.make_config(args.config, args.seed)
+    dev = W.case_to_device(case, "cuda:0")
+    mn = max(1, case.max_nodes)
+    words = (mn + 63) // 64
+    total, batch = case.total_nodes, case.batch
+    dt = tv.dtype_code(dev["q"].dtype)
+    max_path = 16
+    anc = torch.empty((total, words), dtype=torch.int64, device="cuda")
+    depth = torch.empty(total, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dev["q"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_a = tv.tree_verify_attention_workspace_size(batch, total, mn, case.max_prefix, case.hq,
+                                                   case.hkv, case.d, dt)
+    ws_attn = torch.empty(max(ws_a, 1), dtype=torch.uint8, device="cuda")
+    ws_acc = torch.empty(max(tv.tree_accept_workspace_size(batch, case.vocab), 1), dtype=torch.uint8,
+                         device="cuda")
+    acc_out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device="cuda"),
+                   path=torch.empty((batch, max_path), dtype=torch.int32, device="cuda"),
+                   resample_node=torch.empty(batch, dtype=torch.int32, device="cuda"),
+                   resample_token=torch.empty(batch, dtype=torch.int32, device="cuda"),
+                   node_ok=torch.empty(total, dtype=torch.uint8, device="cuda"))
+
+    def attention():
+        tv.tree_verify_attention(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                                 dev["prefix_len"], dev["k_tree"], dev["v_tree"], dev["cu_nodes"],
+                                 anc, mn, case.max_prefix, out=out, want_lse=False,
+                                 workspace=ws_attn if ws_a else None, err=err)
+
+    def step():
+        tv.tree_build_index(dev["parent"], dev["cu_nodes"], mn, anc=anc, depth=depth, err=err)
+        attention()
+        tv.tree_accept(dev["p_target"], dev["p_draft"], dev["token"], dev["u_accept"],
+                       dev["u_resample"], dev["parent"], dev["cu_nodes"], mn, max_path,
+                       outputs=acc_out, workspace=ws_acc, err=err)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise SystemExit(f"device error word {int(err.item())}")
+
+    # eager rate (host launch overhead included)
+    t0 = time.perf_counter()
+    n_eager = min(args.steps, 200)
+    for _ in range(n_eager):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
+
+    # graph-captured step
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    if int(err.item()) != 0:
+        raise SystemExit(f"device error word {int(err.item())}")
+
+    # attention alone: back-to-back launches in one graph, timed with events on its stream
+    reps = args.kernel_reps
+    g_attn = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_attn):
+        for _ in range(reps):
+            attention()
+    g_attn.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g_attn.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        times.append(s_ev.elapsed_time(e_ev) / reps)
+    attn_us = float(np.median(times)) * 1e3
+
+    bytes_, flops = attention_cost(case)
+    if case.dtype == W.DT_F32:
+        t_mem, t_cmp = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (VALU_FP32_PEAK_TFS * 1e12)
+        cbound, cpeak = "alu", VALU_FP32_PEAK_TFS
+    else:
+        t_mem, t_cmp = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)
+        cbound, cpeak = "mfma", MFMA_BF16_PEAK_TFS
+    if t_mem >= t_cmp:
+        ach = bytes_ / (attn_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+    else:
+        ach = flops / (attn_us * 1e-6) / 1e12
+        roof = dict(bound=cbound, achieved=round(ach, 2), peak=cpeak, unit="TFLOP/s",
+                    frac=round(ach / cpeak, 4), traffic=None)
+    roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
+                alg_bytes=int(bytes_), alg_flops=float(flops))
+
+    res = {
+        "metric": "verified tree tokens/s",
+        "value": round(total / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "us_per_step_eager": round(eager_ms * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == W.DT_BF16 else "f32",
+        "data": "synthetic (seeded, HBM-resident; pages' datasets and models are not used)",
+        "config": {"workload": W.CONFIG_NAMES[args.config], "batch": batch, "tree_nodes": total,
+                   "max_prefix": case.max_prefix, "hq": case.hq, "hkv": case.hkv, "head_dim": case.d,
+                   "vocab": case.vocab, "step": "tree_build_index + tree_verify_attention + tree_accept",
+                   "timing": "HIP-graph replay, events on the launch stream",
+                   "wall_s": round(wall, 3)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
