@@ -44,7 +44,7 @@ int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 int launch_attn_combine(const AttnArgs& a, hipStream_t s);
 
-constexpr int kMfmaRowsPerWG = 128;  // 4 waves x 32 rows
+constexpr int kMfmaRowsPerWG = 256;  // 8 waves x 32 rows
 constexpr int kCUs = 256;
 
 }  // namespace tv

@@ -2,48 +2,57 @@
 //
 // Work unit: (sequence b, KV head g, row tile, prefix split).  The rows of one KV
 // head are the G * N_b pairs (node, query head of the group), ordered node-major;
-// a workgroup of 4 wavefronts takes 128 of them, 32 per wavefront.  It streams the
+// a workgroup of 8 wavefronts takes 256 of them, 32 per wavefront.  It streams the
 // prefix of sequence b through the block table, one 64-token paged block at a
 // time, and then the 64-node tiles of the tree that any of its rows can see.  Each
-// tile is staged once in LDS and used by all 128 rows: the shared prefix is read
+// tile is staged once in LDS and used by all 256 rows: the shared prefix is read
 // once per tile for every node of the tree (page "端侧多模态大模型推测解码草稿模型动态剪枝：
 // 详解基于重要性采样的树形验证并行加速策略" (ufo.work/2026/500), §3.2: common prefix kept
 // once and reused; all branches flattened into one launch).
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: a lane
-// then holds 16 keys of a single row per 32-key sub-tile, so the row max and sum
-// need one cross-lane exchange (lane ^ 32) instead of a shuffle tree.  The K rows
+// then holds 16 keys of a single row per 32-key sub-tile, so the row max needs one
+// cross-lane exchange (lane ^ 32) and the row sum none until the end.  The K rows
 // fed to the MFMA are permuted (4-row groups 1<->2 and 5<->6 of every 32) so that
 // the accumulator registers of a lane hold 8 consecutive keys per 16-key step; the
-// probabilities are then packed to bf16 and used directly as the B operand of
-// O^T = V^T P^T, with V stored transposed in LDS so each A operand is one 16-byte
-// read.  Online softmax with running max and sum in fp32 (page
-// "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
-// (ufo.work/2026/537), appendix B: running max m, sum l, rescale by exp(m_old - m_new),
-// bf16 probabilities into the P.V product); the tree mask M_tree (same page, §2.2.2)
-// comes from the 64-bit ancestor word of the row's node for the tile.
+// probabilities are packed to bf16 and used directly as the B operand of
+// O^T = V^T P^T.  V stays in LDS as [key][d]; its A operand comes from the gfx950
+// LDS transpose read (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
+// element i%4 of the 8-byte loads of lanes i/4, 4+i/4, 8+i/4, 12+i/4), so each lane
+// gets 4 consecutive keys of one d per read.  Online softmax with running max and
+// sum in fp32 (page "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存
+// 碎片整理联合加速" (ufo.work/2026/537), appendix B: running max m, sum l, rescale by
+// exp(m_old - m_new), bf16 probabilities into the P.V product); the tree mask M_tree
+// (same page, §2.2.2) comes from the 64-bit ancestor word of the row's node.
 //
-// Tiles are double-buffered: the next tile's global loads are issued into
-// registers before the current tile's matrix work, and written to the other LDS
-// buffer after it; one barrier per tile.  Work indices are remapped so that the
-// workgroups sharing a (sequence, KV head, split) land on the same XCD and hit
-// its L2 for the shared K/V tiles.
+// LDS holds two stages of (K tile, V tile), 64 rows of 256 B each, unpadded; the
+// 16-byte chunks of a row are XOR-swizzled (K by key & 15, V by (key & 3) << 2) so
+// that the MFMA operand reads and the staging writes are free of bank conflicts.
+// Tiles are prefetched two ahead: tile it+2 is loaded into registers during
+// iteration it, tile it+1 (loaded one iteration earlier) is written to the other
+// stage after the matrix work; one barrier per tile.  Work indices are remapped so
+// that the workgroups sharing a (sequence, KV head, split) land on the same XCD and
+// hit its L2 for the shared K/V tiles.
 #include "attn.h"
 
 namespace tv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 128;
-constexpr int kKT = 64;                       // keys per tile
-constexpr int kKStride = kD + 8;              // bf16 per K row in LDS (272 B)
-constexpr int kVStride = kKT + 8;             // bf16 per V^T row in LDS (144 B)
-constexpr int kKBytes = kKT * kKStride * 2;   // 17408
-constexpr int kVBytes = kD * kVStride * 2;    // 18432
-constexpr int kBufBytes = kKBytes + kVBytes;  // 35840
-constexpr int kThreads = 256;
+constexpr int kKT = 64;                           // keys per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTileBytes = kKT * kD * 2;          // 16 KB per K (or V) tile
+constexpr int kStageBytes = 2 * kTileBytes;       // K then V
+constexpr int kSmemBytes = 2 * kStageBytes + 64;  // two stages + small scalars
+constexpr int kChunks = kKT * kD * 2 / 16;        // 16-byte chunks per tile (1024)
+constexpr int kCpt = kChunks / kThreads;          // chunks per thread per tile (2)
 constexpr float kLog2e = 1.4426950408889634f;
+
+static_assert(kMfmaRowsPerWG == kWaves * 32, "row tile is 32 rows per wavefront");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -60,67 +69,54 @@ __device__ __forceinline__ int key_perm(int m) {
   return (swapped << 2) | (m & 3);
 }
 
+// byte offset of (key, 16-byte chunk c) inside a K tile / a V tile
+__device__ __forceinline__ int k_off(int key, int c) { return key * 256 + ((c ^ (key & 15)) << 4); }
+__device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 2)) << 4); }
+
 struct TileSrc {
-  const uint16_t* k;  // first row of the tile (row stride kRowStride elements)
+  const uint16_t* k;  // first row of the tile
   const uint16_t* v;
   long row_stride;    // elements between consecutive keys
   int nvalid;         // rows [0, nvalid) exist; later rows are zero-filled
 };
 
-// Global -> registers for one tile: 4 K chunks and 4x(4 keys) V chunks per thread.
 struct TileRegs {
-  uint4 k[4];
-  uint4 v[4];
+  uint4 k[kCpt];
+  uint4 v[kCpt];
 };
 
 __device__ __forceinline__ void load_tile(const TileSrc& src, int tid, TileRegs& r) {
-  const int dc = tid & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = (tid >> 4) + 16 * i;
-    r.k[i] = key < src.nvalid
-                 ? *reinterpret_cast<const uint4*>(src.k + key * src.row_stride + dc * 8)
-                 : make_uint4(0, 0, 0, 0);
-  }
-  const int kq = tid >> 4;  // keys 4kq .. 4kq+3
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = 4 * kq + i;
-    r.v[i] = key < src.nvalid
-                 ? *reinterpret_cast<const uint4*>(src.v + key * src.row_stride + dc * 8)
-                 : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kCpt; ++i) {
+    const int ci = tid + kThreads * i;
+    const int key = ci >> 4, c = ci & 15;
+    const bool ok = key < src.nvalid;
+    const long off = key * src.row_stride + c * 8;
+    r.k[i] = ok ? *reinterpret_cast<const uint4*>(src.k + off) : make_uint4(0, 0, 0, 0);
+    r.v[i] = ok ? *reinterpret_cast<const uint4*>(src.v + off) : make_uint4(0, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_tile(char* buf, int tid, const TileRegs& r) {
-  const int dc = tid & 15;
+__device__ __forceinline__ void store_tile(char* stage, int tid, const TileRegs& r) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = (tid >> 4) + 16 * i;
-    *reinterpret_cast<uint4*>(buf + key * (kKStride * 2) + dc * 16) = r.k[i];
-  }
-  // V^T[d][key]: for each of the 8 d of this chunk, the 4 keys 4kq..4kq+3
-  char* vt = buf + kKBytes;
-  const int kq = tid >> 4;
-  const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-  const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-  const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
-  const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // d = 8dc + 2j (low halves) and 8dc + 2j + 1 (high halves)
-    const uint2 lo = make_uint2((w0[j] & 0xffffu) | (w1[j] << 16), (w2[j] & 0xffffu) | (w3[j] << 16));
-    const uint2 hi = make_uint2((w0[j] >> 16) | (w1[j] & 0xffff0000u),
-                                (w2[j] >> 16) | (w3[j] & 0xffff0000u));
-    const int d = 8 * dc + 2 * j;
-    *reinterpret_cast<uint2*>(vt + d * (kVStride * 2) + kq * 8) = lo;
-    *reinterpret_cast<uint2*>(vt + (d + 1) * (kVStride * 2) + kq * 8) = hi;
+  for (int i = 0; i < kCpt; ++i) {
+    const int ci = tid + kThreads * i;
+    const int key = ci >> 4, c = ci & 15;
+    *reinterpret_cast<uint4*>(stage + k_off(key, c)) = r.k[i];
+    *reinterpret_cast<uint4*>(stage + kTileBytes + v_off(key, c)) = r.v[i];
   }
 }
 
-__global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// LDS transpose read of 4 bf16 (p points into the workgroup's LDS)
+__device__ __forceinline__ bf16x4_t ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
+
+__global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ uint32_t s_tree_mask;
+  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);
 
   // ---- work item (XCD-aware: consecutive work indices share an XCD)
   const int per_xcd = gridDim.x / 8;
@@ -155,26 +151,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
   const int n_prefix_tiles = max(0, kb1 - kb0);
   const bool do_tree = split == a.splits - 1;
 
-  // ---- which 64-node tree tiles any row of this workgroup can see
-  if (tid == 0) s_tree_mask = 0;
-  __syncthreads();
-  const int ntw = (count + 63) / 64;
-  if (do_tree) {
-    const int lo = r0 / a.group;
-    const int hi = (min(rows, r0 + kMfmaRowsPerWG) - 1) / a.group;
-    const int pairs_n = (hi - lo + 1) * ntw;
-    uint32_t m = 0;
-    for (int i = tid; i < pairs_n; i += kThreads) {
-      const int nd = lo + i / ntw, t = i % ntw;
-      if (a.anc[static_cast<long>(n0 + nd) * a.words + t] != 0) m |= 1u << t;
-    }
-    if (m) atomicOr(&s_tree_mask, m);
-  }
-  __syncthreads();
-  const uint32_t tree_mask = do_tree ? s_tree_mask : 0u;
-  const int n_tiles = n_prefix_tiles + __popc(tree_mask);
-
-  // ---- this lane's row and its Q fragment (B operand of S^T = K Q^T)
+  // ---- this lane's row and its Q fragment (B operand of S^T = K Q^T); issued early
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
   const int r = r0 + wave * 32 + col;
@@ -189,19 +166,48 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
   for (int s = 0; s < 8; ++s)
     qf[s] = as_bf16x8(row_ok ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0));
 
+  // ---- which 64-node tree tiles any row of this workgroup can see
+  if (tid == 0) *s_tree_mask = 0;
+  __syncthreads();
+  const int ntw = (count + 63) / 64;
+  if (do_tree) {
+    const int lo = r0 / a.group;
+    const int hi = (min(rows, r0 + kMfmaRowsPerWG) - 1) / a.group;
+    const int pairs_n = (hi - lo + 1) * ntw;
+    uint32_t m = 0;
+    for (int i = tid; i < pairs_n; i += kThreads) {
+      const int nd = lo + i / ntw, t = i % ntw;
+      if (a.anc[static_cast<long>(n0 + nd) * a.words + t] != 0) m |= 1u << t;
+    }
+    if (m) atomicOr(s_tree_mask, m);
+  }
+  __syncthreads();
+  const uint32_t tree_mask = do_tree ? *s_tree_mask : 0u;
+  const int n_tiles = n_prefix_tiles + __popc(tree_mask);
+
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
   const uint16_t* kt = static_cast<const uint16_t*>(a.k_tree);
   const uint16_t* vt = static_cast<const uint16_t*>(a.v_tree);
 
-  // tile it -> source rows, and (for masking) its kind and base index
-  auto tile_src = [&](int it, int& kind, int& base) -> TileSrc {
-    TileSrc s;
+  // tile it -> kind (0 prefix block, 1 tree tile) and base (first key, or tree word)
+  auto tile_kind = [&](int it, int& kind, int& base) {
     if (it < n_prefix_tiles) {
-      const int kb = kb0 + it;
-      int blk = a.block_table[static_cast<long>(b) * a.max_blocks + kb];
       kind = 0;
-      base = kb * kKT;
+      base = (kb0 + it) * kKT;
+    } else {
+      uint32_t m = tree_mask;
+      for (int j = it - n_prefix_tiles; j > 0; --j) m &= m - 1;
+      kind = 1;
+      base = __ffs(m) - 1;
+    }
+  };
+  auto tile_src = [&](int it) -> TileSrc {
+    int kind, base;
+    tile_kind(it, kind, base);
+    TileSrc s;
+    if (kind == 0) {
+      const int blk = a.block_table[static_cast<long>(b) * a.max_blocks + base / kKT];
       if (blk < 0 || blk >= a.num_blocks) {
         if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
         s.k = kc;
@@ -216,16 +222,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
       s.row_stride = kD;
       s.nvalid = min(kKT, plen - base);
     } else {
-      uint32_t m = tree_mask;
-      for (int j = it - n_prefix_tiles; j > 0; --j) m &= m - 1;
-      const int t = __ffs(m) - 1;
-      kind = 1;
-      base = t;
-      const long off = (static_cast<long>(n0 + t * 64) * a.hkv + g) * kD;
+      const long off = (static_cast<long>(n0 + base * 64) * a.hkv + g) * kD;
       s.k = kt + off;
       s.v = vt + off;
       s.row_stride = static_cast<long>(a.hkv) * kD;
-      s.nvalid = min(64, count - t * 64);
+      s.nvalid = min(64, count - base * 64);
     }
     return s;
   };
@@ -238,94 +239,121 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
   const int krow0 = key_perm(col);
   const uint64_t* anc_row = a.anc + static_cast<long>(n0 + node) * a.words;
 
-  TileRegs regs;
-  int kind_cur = 0, base_cur = 0;
-  if (n_tiles > 0) {
-    TileSrc s0 = tile_src(0, kind_cur, base_cur);
-    load_tile(s0, tid, regs);
-    store_tile(smem, tid, regs);
-  }
-  __syncthreads();
+  // per-lane LDS offsets of the S^T A operand (K) for the two 32-key sub-tiles
+  int k_base[2];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) k_base[sg] = (32 * sg + krow0) * 256;
+  const int k_xor = krow0 & 15;  // (32 sg + krow0) & 15 == krow0 & 15
+  // per-lane LDS offsets of the transposed V reads, one per 32-wide d-tile
+  const int grp = lane >> 4, jg = lane & 15, hh = grp >> 1;
+  const int low = 2 * (grp & 1) + ((jg & 3) >> 1);
+  int v_base[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    v_base[dt] = kTileBytes + (8 * hh + (jg >> 2)) * 256 + ((((dt ^ (jg >> 2)) << 2) + low) << 4) +
+                 8 * (jg & 1);
 
-  for (int it = 0; it < n_tiles; ++it) {
-    char* buf = smem + (it & 1) * kBufBytes;
-    int kind_nxt = 0, base_nxt = 0;
-    const bool more = it + 1 < n_tiles;
-    if (more) {
-      TileSrc sn = tile_src(it + 1, kind_nxt, base_nxt);
-      load_tile(sn, tid, regs);
+  auto compute = [&](const char* stage, int kind, int base) {
+    // S^T for two 32-key sub-tiles
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+      sacc[sg] = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 2 * s + half;
+        const bf16x8_t kf =
+            as_bf16x8(*reinterpret_cast<const uint4*>(stage + k_base[sg] + ((c ^ k_xor) << 4)));
+        sacc[sg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sg], 0, 0, 0);
+      }
     }
-    if (wave_live) {
-      // S^T for two 32-key sub-tiles
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg) {
-        sacc[sg] = f32x16_t{};
-        const char* kr = buf + (32 * sg + krow0) * (kKStride * 2) + half * 16;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(kr + s * 32));
-          sacc[sg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sg], 0, 0, 0);
-        }
-      }
-      // mask: key index of register v of sub-tile sg is 32sg + 16(v/8) + 8*half + v%8
+    // mask: key index of register v of sub-tile sg is 32sg + 16(v/8) + 8*half + v%8
+    bool full = kind == 0 && plen - base >= kKT;
+    if (!full) {
       uint64_t vis;
-      if (kind_cur == 0) {
-        const int nv = plen - base_cur;  // keys [0, nv) of this block are in the prefix
-        vis = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+      if (kind == 0) {
+        const int nv = plen - base;
+        vis = (1ull << nv) - 1ull;  // 0 < nv < 64 here
       } else {
-        vis = row_ok ? anc_row[base_cur] : 0ull;
+        vis = row_ok ? anc_row[base] : 0ull;
       }
-      float mx = -INFINITY;
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kk = 32 * sg + 16 * (v >> 3) + 8 * half + (v & 7);
-          const float sv = ((vis >> kk) & 1ull) ? sacc[sg][v] : -INFINITY;
-          sacc[sg][v] = sv;
-          mx = fmaxf(mx, sv);
+          sacc[sg][v] = ((vis >> kk) & 1ull) ? sacc[sg][v] : -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[sg][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float mc = m_use * c2;
+    if (__ballot(m_new != m_run)) {  // rescale only when some row's max moved
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      const float mc = m_use * c2;
-      float psum = 0.0f;
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[sg][v] * c2 - mc);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[sg][v + 1] * c2 - mc);
-          psum += p0 + p1;
-          pk[sg][v >> 1] = pack2_bf16(p0, p1);
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] *= alpha;
-      // O^T += V^T P^T, 16 keys per step
+    }
+    m_run = m_new;
+    float psum = 0.0f;
+    uint32_t pk[2][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sg = j >> 1, vb = (j & 1) * 4;
-        const uint4 pw = make_uint4(pk[sg][vb], pk[sg][vb + 1], pk[sg][vb + 2], pk[sg][vb + 3]);
-        const bf16x8_t pf = as_bf16x8(pw);
-        const char* vr = buf + kKBytes + col * (kVStride * 2) + (16 * j + 8 * half) * 2;
+    for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const uint4*>(vr + dt * 32 * (kVStride * 2)));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
-        }
+      for (int v = 0; v < 16; v += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sacc[sg][v] * c2 - mc);
+        const float p1 = __builtin_amdgcn_exp2f(sacc[sg][v + 1] * c2 - mc);
+        psum += p0 + p1;
+        pk[sg][v >> 1] = pack2_bf16(p0, p1);
+      }
+    l_run += psum;
+    // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sg = j >> 1, vb = (j & 1) * 4;
+      const bf16x8_t pf =
+          as_bf16x8(make_uint4(pk[sg][vb], pk[sg][vb + 1], pk[sg][vb + 2], pk[sg][vb + 3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const char* p = stage + v_base[dt] + 16 * j * 256;
+        const bf16x4_t lo = ds_read_tr(p);
+        const bf16x4_t hi = ds_read_tr(p + 4 * 256);
+        const bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
       }
     }
-    if (more) store_tile(smem + ((it + 1) & 1) * kBufBytes, tid, regs);
-    kind_cur = kind_nxt;
-    base_cur = base_nxt;
+  };
+
+  TileRegs ra, rb;
+  if (n_tiles > 0) {
+    load_tile(tile_src(0), tid, ra);
+    if (n_tiles > 1) load_tile(tile_src(1), tid, rb);
+    store_tile(smem, tid, ra);
+  }
+  __syncthreads();
+
+  // iteration it reads stage it&1; register set ra holds even tiles, rb odd tiles
+  auto step = [&](int it, TileRegs& mine, TileRegs& next) {
+    if (it + 2 < n_tiles) load_tile(tile_src(it + 2), tid, mine);
+    if (wave_live) {
+      int kind, base;
+      tile_kind(it, kind, base);
+      compute(smem + (it & 1) * kStageBytes, kind, base);
+    }
+    if (it + 1 < n_tiles) store_tile(smem + ((it + 1) & 1) * kStageBytes, tid, next);
     __syncthreads();
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(it, ra, rb);
+    if (it + 1 < n_tiles) step(it + 1, rb, ra);
   }
 
   if (!row_ok) return;
@@ -363,12 +391,12 @@ __global__ void __launch_bounds__(kThreads, 2) k_attn_mfma(AttnArgs a) {
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBufBytes);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
     attr_set = true;
   }
   const int grid = 8 * ceil_div(a.total_work, 8);
-  hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(kThreads), 2 * kBufBytes, s, a);
+  hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
   return check_launch("tree_verify_attention/mfma");
 }
 
