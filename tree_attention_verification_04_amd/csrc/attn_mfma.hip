@@ -85,23 +85,28 @@ struct TileRegs {
   uint4 v[kCpt];
 };
 
+// Rows at or past nvalid are read from row nvalid - 1 (always inside the source
+// array) and zeroed when the tile is written to LDS, so the loads need no branch.
 __device__ __forceinline__ void load_tile(const TileSrc& src, int tid, TileRegs& r) {
 #pragma unroll
   for (int i = 0; i < kCpt; ++i) {
     const int ci = tid + kThreads * i;
-    const int key = ci >> 4, c = ci & 15;
-    const bool ok = key < src.nvalid;
+    const int key = min(ci >> 4, max(src.nvalid - 1, 0)), c = ci & 15;
     const long off = key * src.row_stride + c * 8;
-    r.k[i] = ok ? *reinterpret_cast<const uint4*>(src.k + off) : make_uint4(0, 0, 0, 0);
-    r.v[i] = ok ? *reinterpret_cast<const uint4*>(src.v + off) : make_uint4(0, 0, 0, 0);
+    r.k[i] = *reinterpret_cast<const uint4*>(src.k + off);
+    r.v[i] = *reinterpret_cast<const uint4*>(src.v + off);
   }
 }
 
-__device__ __forceinline__ void store_tile(char* stage, int tid, const TileRegs& r) {
+__device__ __forceinline__ void store_tile(char* stage, int tid, TileRegs& r, int nvalid) {
 #pragma unroll
   for (int i = 0; i < kCpt; ++i) {
     const int ci = tid + kThreads * i;
     const int key = ci >> 4, c = ci & 15;
+    if (nvalid < kKT && key >= nvalid) {  // nvalid is uniform: the branch is rare
+      r.k[i] = make_uint4(0, 0, 0, 0);
+      r.v[i] = make_uint4(0, 0, 0, 0);
+    }
     *reinterpret_cast<uint4*>(stage + k_off(key, c)) = r.k[i];
     *reinterpret_cast<uint4*>(stage + kTileBytes + v_off(key, c)) = r.v[i];
   }
@@ -202,12 +207,16 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
       base = __ffs(m) - 1;
     }
   };
+  // block-table entries through the scalar (constant) path: uniform, read-only
+  const __attribute__((address_space(4))) int32_t* bt_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
+      static_cast<long>(b) * a.max_blocks;
   auto tile_src = [&](int it) -> TileSrc {
     int kind, base;
     tile_kind(it, kind, base);
     TileSrc s;
     if (kind == 0) {
-      const int blk = a.block_table[static_cast<long>(b) * a.max_blocks + base / kKT];
+      const int blk = bt_row[base / kKT];
       if (blk < 0 || blk >= a.num_blocks) {
         if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
         s.k = kc;
@@ -253,7 +262,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     v_base[dt] = kTileBytes + (8 * hh + (jg >> 2)) * 256 + ((((dt ^ (jg >> 2)) << 2) + low) << 4) +
                  8 * (jg & 1);
 
-  auto compute = [&](const char* stage, int kind, int base) {
+  auto compute = [&](const char* stage, int kind, int base, uint64_t vis_tree) {
     // S^T for two 32-key sub-tiles
     f32x16_t sacc[2];
 #pragma unroll
@@ -275,7 +284,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
         const int nv = plen - base;
         vis = (1ull << nv) - 1ull;  // 0 < nv < 64 here
       } else {
-        vis = row_ok ? anc_row[base] : 0ull;
+        vis = vis_tree;
       }
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg)
@@ -332,28 +341,37 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     }
   };
 
+  // Loads are issued on every path (past the last tile they re-read the last
+  // tile), so that the wait before each LDS write covers only the older set.
   TileRegs ra, rb;
+  int nv_a = 0, nv_b = 0;  // valid rows of the tiles held in ra / rb
   if (n_tiles > 0) {
-    load_tile(tile_src(0), tid, ra);
-    if (n_tiles > 1) load_tile(tile_src(1), tid, rb);
-    store_tile(smem, tid, ra);
+    const TileSrc s0 = tile_src(0);
+    load_tile(s0, tid, ra);
+    nv_a = s0.nvalid;
+    const TileSrc s1 = tile_src(min(1, n_tiles - 1));
+    load_tile(s1, tid, rb);
+    nv_b = s1.nvalid;
+    store_tile(smem, tid, ra, nv_a);
   }
   __syncthreads();
 
   // iteration it reads stage it&1; register set ra holds even tiles, rb odd tiles
-  auto step = [&](int it, TileRegs& mine, TileRegs& next) {
-    if (it + 2 < n_tiles) load_tile(tile_src(it + 2), tid, mine);
-    if (wave_live) {
-      int kind, base;
-      tile_kind(it, kind, base);
-      compute(smem + (it & 1) * kStageBytes, kind, base);
-    }
-    if (it + 1 < n_tiles) store_tile(smem + ((it + 1) & 1) * kStageBytes, tid, next);
+  auto step = [&](int it, TileRegs& mine, int& nv_mine, TileRegs& next, int nv_next) {
+    int kind, base;
+    tile_kind(it, kind, base);
+    uint64_t vis_tree = 0;
+    if (kind == 1) vis_tree = anc_row[base];  // before the prefetch, so its wait is short
+    const TileSrc sn = tile_src(min(it + 2, n_tiles - 1));
+    load_tile(sn, tid, mine);
+    nv_mine = sn.nvalid;
+    if (wave_live) compute(smem + (it & 1) * kStageBytes, kind, base, row_ok ? vis_tree : 0ull);
+    if (it + 1 < n_tiles) store_tile(smem + ((it + 1) & 1) * kStageBytes, tid, next, nv_next);
     __syncthreads();
   };
   for (int it = 0; it < n_tiles; it += 2) {
-    step(it, ra, rb);
-    if (it + 1 < n_tiles) step(it + 1, rb, ra);
+    step(it, ra, nv_a, rb, nv_b);
+    if (it + 1 < n_tiles) step(it + 1, rb, nv_b, ra, nv_a);
   }
 
   if (!row_ok) return;
