@@ -47,7 +47,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileBytes = kKT * kD * 2;          // 16 KB per K (or V) tile
 constexpr int kStageBytes = 2 * kTileBytes;       // K then V
-constexpr int kSmemBytes = 2 * kStageBytes + 64;  // two stages + small scalars
+constexpr int kSmemBytes = 3 * kStageBytes + 64;  // three stages + small scalars
 constexpr int kChunks = kKT * kD * 2 / 16;        // 16-byte chunks per tile (1024)
 constexpr int kCpt = kChunks / kThreads;          // chunks per thread per tile (2)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -121,7 +121,7 @@ __device__ __forceinline__ bf16x4_t ds_read_tr(const char* p) {
 
 __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);
+  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + 3 * kStageBytes);
 
   // ---- work item (XCD-aware: consecutive work indices share an XCD)
   const int per_xcd = gridDim.x / 8;
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   const uint16_t* vt = static_cast<const uint16_t*>(a.v_tree);
 
   // tile it -> kind (0 prefix block, 1 tree tile) and base (first key, or tree word)
-  auto tile_kind = [&](int it, int& kind, int& base) {
+  auto tile_kind = [&](int it, int& kind, int& base) __attribute__((always_inline)) {
     if (it < n_prefix_tiles) {
       kind = 0;
       base = (kb0 + it) * kKT;
@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
       static_cast<long>(b) * a.max_blocks;
-  auto tile_src = [&](int it) -> TileSrc {
+  auto tile_src = [&](int it) __attribute__((always_inline)) -> TileSrc {
     int kind, base;
     tile_kind(it, kind, base);
     TileSrc s;
@@ -262,9 +262,12 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     v_base[dt] = kTileBytes + (8 * hh + (jg >> 2)) * 256 + ((((dt ^ (jg >> 2)) << 2) + low) << 4) +
                  8 * (jg & 1);
 
-  auto compute = [&](const char* stage, int kind, int base, uint64_t vis_tree) {
-    // S^T for two 32-key sub-tiles
-    f32x16_t sacc[2];
+  f32x16_t sacc[2];   // S^T of the tile between its score MFMAs and its softmax
+  uint32_t pk[2][8];  // bf16 probabilities between the softmax and the P.V MFMAs
+  uint64_t vis_tree = 0;
+
+  // scores of tile it: S^T = K Q^T
+  auto mfma_scores = [&](const char* stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg) {
       sacc[sg] = f32x16_t{};
@@ -276,23 +279,40 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
         sacc[sg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sg], 0, 0, 0);
       }
     }
-    // mask: key index of register v of sub-tile sg is 32sg + 16(v/8) + 8*half + v%8
-    bool full = kind == 0 && plen - base >= kKT;
-    if (!full) {
-      uint64_t vis;
-      if (kind == 0) {
-        const int nv = plen - base;
-        vis = (1ull << nv) - 1ull;  // 0 < nv < 64 here
-      } else {
-        vis = vis_tree;
+  };
+  // O^T += V^T P^T for the tile whose probabilities are in pk
+  auto mfma_pv = [&](const char* stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sg = j >> 1, vb = (j & 1) * 4;
+      const bf16x8_t pf =
+          as_bf16x8(make_uint4(pk[sg][vb], pk[sg][vb + 1], pk[sg][vb + 2], pk[sg][vb + 3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const char* p = stage + v_base[dt] + 16 * j * 256;
+        const bf16x4_t lo = ds_read_tr(p);
+        const bf16x4_t hi = ds_read_tr(p + 4 * 256);
+        const bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
       }
+    }
+  };
+  // mask, online-softmax update, bf16 probabilities of tile it
+  auto softmax = [&](int kind, int base) __attribute__((always_inline)) {
+    // key index of register v of sub-tile sg is 32sg + 16(v/8) + 8*half + v%8
+    const bool full = kind == 0 && plen - base >= kKT;
+    if (!full) {
+      const uint64_t vis = kind == 0 ? ((1ull << (plen - base)) - 1ull) : (row_ok ? vis_tree : 0ull);
+      // the 32 keys this lane holds, compressed so that register (sg, v) is bit 16sg + v
+      const uint32_t lo = static_cast<uint32_t>(vis), hi = static_cast<uint32_t>(vis >> 32);
+      const int sh = 8 * half;
+      const uint32_t w = ((lo >> sh) & 0xffu) | (((lo >> (16 + sh)) & 0xffu) << 8) |
+                         (((hi >> sh) & 0xffu) << 16) | (((hi >> (16 + sh)) & 0xffu) << 24);
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = 32 * sg + 16 * (v >> 3) + 8 * half + (v & 7);
-          sacc[sg][v] = ((vis >> kk) & 1ull) ? sacc[sg][v] : -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          sacc[sg][v] = ((w >> (16 * sg + v)) & 1u) ? sacc[sg][v] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -313,7 +333,6 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     }
     m_run = m_new;
     float psum = 0.0f;
-    uint32_t pk[2][8];
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
@@ -324,54 +343,92 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
         pk[sg][v >> 1] = pack2_bf16(p0, p1);
       }
     l_run += psum;
-    // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int sg = j >> 1, vb = (j & 1) * 4;
-      const bf16x8_t pf =
-          as_bf16x8(make_uint4(pk[sg][vb], pk[sg][vb + 1], pk[sg][vb + 2], pk[sg][vb + 3]));
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const char* p = stage + v_base[dt] + 16 * j * 256;
-        const bf16x4_t lo = ds_read_tr(p);
-        const bf16x4_t hi = ds_read_tr(p + 4 * 256);
-        const bf16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
-      }
+  };
+
+  // ---- ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) sit on the
+  // same four SIMDs, one of each per SIMD.  Phases alternate: while one group
+  // runs its matrix phase (P.V of tile i-1, then the scores of tile i) the other
+  // runs the softmax of its previous tile on the vector ALU, so the two kinds of
+  // work overlap on every SIMD.  Group A runs the matrix phase of tile i in phase
+  // 2i and the softmax of tile i in phase 2i+1; group B runs one phase later.
+  // Tile i lives in LDS stage i % 3 from phase 2i-2 (written) to phase 2i+3 (last
+  // read).  Phase 2i writes tile i+1 from its registers; phase 2i+1 issues the
+  // loads of tile i+3 into the register set just freed.  One barrier per phase.
+  const bool group_b = wave >= 4;
+  TileRegs r0s, r1s;       // register sets: set (i % 2) carries tiles i, i+2, ...
+  int nv0 = 0, nv1 = 0;
+  auto stage_of = [&](int i) __attribute__((always_inline)) -> char* { return smem + (i % 3) * kStageBytes; };
+  auto matrix_phase = [&](int i) __attribute__((always_inline)) {  // P.V of tile i-1, scores of tile i
+    if (i >= 1) mfma_pv(stage_of(i - 1));
+    __builtin_amdgcn_sched_barrier(0);  // keep the two MFMA chains' operand reads apart
+    if (i < n_tiles) {
+      int kind, base;
+      tile_kind(i, kind, base);
+      if (kind == 1) vis_tree = anc_row[base];
+      mfma_scores(stage_of(i));
+    }
+  };
+  auto vector_phase = [&](int i) __attribute__((always_inline)) {
+    if (i >= 0 && i < n_tiles) {
+      int kind, base;
+      tile_kind(i, kind, base);
+      softmax(kind, base);
+    }
+  };
+  auto compute_phase = [&](int p) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    if (!group_b) {
+      if ((p & 1) == 0) matrix_phase(p >> 1);
+      else vector_phase(p >> 1);
+    } else {
+      if (p & 1) matrix_phase(p >> 1);
+      else vector_phase((p >> 1) - 1);
     }
   };
 
-  // Loads are issued on every path (past the last tile they re-read the last
-  // tile), so that the wait before each LDS write covers only the older set.
-  TileRegs ra, rb;
-  int nv_a = 0, nv_b = 0;  // valid rows of the tiles held in ra / rb
   if (n_tiles > 0) {
     const TileSrc s0 = tile_src(0);
-    load_tile(s0, tid, ra);
-    nv_a = s0.nvalid;
+    load_tile(s0, tid, r0s);
+    nv0 = s0.nvalid;
     const TileSrc s1 = tile_src(min(1, n_tiles - 1));
-    load_tile(s1, tid, rb);
-    nv_b = s1.nvalid;
-    store_tile(smem, tid, ra, nv_a);
-  }
-  __syncthreads();
-
-  // iteration it reads stage it&1; register set ra holds even tiles, rb odd tiles
-  auto step = [&](int it, TileRegs& mine, int& nv_mine, TileRegs& next, int nv_next) {
-    int kind, base;
-    tile_kind(it, kind, base);
-    uint64_t vis_tree = 0;
-    if (kind == 1) vis_tree = anc_row[base];  // before the prefetch, so its wait is short
-    const TileSrc sn = tile_src(min(it + 2, n_tiles - 1));
-    load_tile(sn, tid, mine);
-    nv_mine = sn.nvalid;
-    if (wave_live) compute(smem + (it & 1) * kStageBytes, kind, base, row_ok ? vis_tree : 0ull);
-    if (it + 1 < n_tiles) store_tile(smem + ((it + 1) & 1) * kStageBytes, tid, next, nv_next);
+    load_tile(s1, tid, r1s);
+    nv1 = s1.nvalid;
+    store_tile(stage_of(0), tid, r0s, nv0);
+    const TileSrc s2 = tile_src(min(2, n_tiles - 1));
+    load_tile(s2, tid, r0s);
+    nv0 = s2.nvalid;
     __syncthreads();
-  };
-  for (int it = 0; it < n_tiles; it += 2) {
-    step(it, ra, nv_a, rb, nv_b);
-    if (it + 1 < n_tiles) step(it + 1, rb, nv_b, ra, nv_a);
+    // phases 4k .. 4k+3 cover tiles i = 2k (phases 4k, 4k+1) and 2k+1
+    for (int k = 0; 4 * k <= 2 * n_tiles + 1; ++k) {
+      const int i0 = 2 * k, i1 = 2 * k + 1;
+      // phase 4k (= 2*i0): write tile i0+1 (set 1)
+      if (i0 + 1 < n_tiles) store_tile(stage_of(i0 + 1), tid, r1s, nv1);
+      compute_phase(4 * k);
+      __syncthreads();
+      if (4 * k + 1 > 2 * n_tiles + 1) break;
+      // phase 4k+1: loads of tile i0+3 into set 1
+      {
+        const TileSrc sn = tile_src(min(i0 + 3, n_tiles - 1));
+        load_tile(sn, tid, r1s);
+        nv1 = sn.nvalid;
+      }
+      compute_phase(4 * k + 1);
+      __syncthreads();
+      if (4 * k + 2 > 2 * n_tiles + 1) break;
+      // phase 4k+2 (= 2*i1): write tile i1+1 (set 0)
+      if (i1 + 1 < n_tiles) store_tile(stage_of(i1 + 1), tid, r0s, nv0);
+      compute_phase(4 * k + 2);
+      __syncthreads();
+      if (4 * k + 3 > 2 * n_tiles + 1) break;
+      // phase 4k+3: loads of tile i1+3 into set 0
+      {
+        const TileSrc sn = tile_src(min(i1 + 3, n_tiles - 1));
+        load_tile(sn, tid, r0s);
+        nv0 = sn.nvalid;
+      }
+      compute_phase(4 * k + 3);
+      __syncthreads();
+    }
   }
 
   if (!row_ok) return;
