@@ -47,7 +47,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileBytes = kKT * kD * 2;          // 16 KB per K (or V) tile
 constexpr int kStageBytes = 2 * kTileBytes;       // K then V
-constexpr int kSmemBytes = 3 * kStageBytes + 64;  // three stages + small scalars
+constexpr int kAncBytes = kMfmaRowsPerWG * 8;       // ancestor words of the rows, per stage
+constexpr int kAncOff = 3 * kStageBytes;
+constexpr int kSmemBytes = 3 * kStageBytes + 3 * kAncBytes + 64;  // three stages + scalars
 constexpr int kChunks = kKT * kD * 2 / 16;        // 16-byte chunks per tile (1024)
 constexpr int kCpt = kChunks / kThreads;          // chunks per thread per tile (2)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -74,15 +76,17 @@ __device__ __forceinline__ int k_off(int key, int c) { return key * 256 + ((c ^ 
 __device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 2)) << 4); }
 
 struct TileSrc {
-  const uint16_t* k;  // first row of the tile
+  const uint16_t* k;    // first row of the tile
   const uint16_t* v;
-  long row_stride;    // elements between consecutive keys
-  int nvalid;         // rows [0, nvalid) exist; later rows are zero-filled
+  long row_stride;      // elements between consecutive keys
+  int nvalid;           // rows [0, nvalid) exist; later rows are zero-filled
+  const uint64_t* anc;  // ancestor word of this thread's row for the tile (tree tiles)
 };
 
 struct TileRegs {
   uint4 k[kCpt];
   uint4 v[kCpt];
+  uint64_t anc;
 };
 
 // Rows at or past nvalid are read from row nvalid - 1 (always inside the source
@@ -96,9 +100,13 @@ __device__ __forceinline__ void load_tile(const TileSrc& src, int tid, TileRegs&
     r.k[i] = *reinterpret_cast<const uint4*>(src.k + off);
     r.v[i] = *reinterpret_cast<const uint4*>(src.v + off);
   }
+  r.anc = *src.anc;
 }
 
-__device__ __forceinline__ void store_tile(char* stage, int tid, TileRegs& r, int nvalid) {
+// The ancestor words of the workgroup's 256 rows go to a small LDS slot per stage.
+__device__ __forceinline__ void store_tile(char* stage, uint64_t* anc_slot, int tid, TileRegs& r,
+                                           int nvalid) {
+  if (tid < kMfmaRowsPerWG) anc_slot[tid] = r.anc;
 #pragma unroll
   for (int i = 0; i < kCpt; ++i) {
     const int ci = tid + kThreads * i;
@@ -121,7 +129,8 @@ __device__ __forceinline__ bf16x4_t ds_read_tr(const char* p) {
 
 __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + 3 * kStageBytes);
+  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kAncOff + 3 * kAncBytes);
+  int* s_simd_slots = reinterpret_cast<int*>(smem + kAncOff + 3 * kAncBytes + 16);  // [4]
 
   // ---- work item (XCD-aware: consecutive work indices share an XCD)
   const int per_xcd = gridDim.x / 8;
@@ -173,6 +182,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
 
   // ---- which 64-node tree tiles any row of this workgroup can see
   if (tid == 0) *s_tree_mask = 0;
+  if (tid < 4) s_simd_slots[tid] = 0;
   __syncthreads();
   const int ntw = (count + 63) / 64;
   if (do_tree) {
@@ -211,10 +221,14 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
       static_cast<long>(b) * a.max_blocks;
+  // the ancestor-word row of this thread's staging row (tid & 255 of the 256 rows)
+  const int stage_node = min((r0 + (tid & (kMfmaRowsPerWG - 1))) / a.group, count - 1);
+  const uint64_t* stage_anc = a.anc + static_cast<long>(n0 + stage_node) * a.words;
   auto tile_src = [&](int it) __attribute__((always_inline)) -> TileSrc {
     int kind, base;
     tile_kind(it, kind, base);
     TileSrc s;
+    s.anc = stage_anc + (kind == 1 ? base : 0);
     if (kind == 0) {
       const int blk = bt_row[base / kKT];
       if (blk < 0 || blk >= a.num_blocks) {
@@ -246,7 +260,6 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float c2 = a.scale * kLog2e;
   const int krow0 = key_perm(col);
-  const uint64_t* anc_row = a.anc + static_cast<long>(n0 + node) * a.words;
 
   // per-lane LDS offsets of the S^T A operand (K) for the two 32-key sub-tiles
   int k_base[2];
@@ -264,7 +277,6 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
 
   f32x16_t sacc[2];   // S^T of the tile between its score MFMAs and its softmax
   uint32_t pk[2][8];  // bf16 probabilities between the softmax and the P.V MFMAs
-  uint64_t vis_tree = 0;
 
   // scores of tile it: S^T = K Q^T
   auto mfma_scores = [&](const char* stage) __attribute__((always_inline)) {
@@ -279,6 +291,14 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
         sacc[sg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sg], 0, 0, 0);
       }
     }
+    // keep the K reads four MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
   // O^T += V^T P^T for the tile whose probabilities are in pk
   auto mfma_pv = [&](const char* stage) __attribute__((always_inline)) {
@@ -296,13 +316,22 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[dt], 0, 0, 0);
       }
     }
+    // keep the transposed V reads four MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // mask, online-softmax update, bf16 probabilities of tile it
-  auto softmax = [&](int kind, int base) __attribute__((always_inline)) {
+  auto softmax = [&](int kind, int base, const uint64_t* anc_slot) __attribute__((always_inline)) {
     // key index of register v of sub-tile sg is 32sg + 16(v/8) + 8*half + v%8
     const bool full = kind == 0 && plen - base >= kKT;
     if (!full) {
-      const uint64_t vis = kind == 0 ? ((1ull << (plen - base)) - 1ull) : (row_ok ? vis_tree : 0ull);
+      const uint64_t vis = kind == 0 ? ((1ull << (plen - base)) - 1ull)
+                                     : (row_ok ? anc_slot[wave * 32 + col] : 0ull);
       // the 32 keys this lane holds, compressed so that register (sg, v) is bit 16sg + v
       const uint32_t lo = static_cast<uint32_t>(vis), hi = static_cast<uint32_t>(vis >> 32);
       const int sh = 8 * half;
@@ -354,17 +383,21 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   // Tile i lives in LDS stage i % 3 from phase 2i-2 (written) to phase 2i+3 (last
   // read).  Phase 2i writes tile i+1 from its registers; phase 2i+1 issues the
   // loads of tile i+3 into the register set just freed.  One barrier per phase.
-  const bool group_b = wave >= 4;
+  // One wave of each group per SIMD: waves take turns per SIMD (SIMD id from the
+  // HW_ID register, bits 5:4); any assignment is correct, this one overlaps best.
+  int slot = 0;
+  if (lane == 0) slot = atomicAdd(&s_simd_slots[__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3], 1);
+  const bool group_b = __shfl(slot, 0, 64) & 1;
   TileRegs r0s, r1s;       // register sets: set (i % 2) carries tiles i, i+2, ...
   int nv0 = 0, nv1 = 0;
   auto stage_of = [&](int i) __attribute__((always_inline)) -> char* { return smem + (i % 3) * kStageBytes; };
+  auto anc_of = [&](int i) __attribute__((always_inline)) -> uint64_t* {
+    return reinterpret_cast<uint64_t*>(smem + kAncOff + (i % 3) * kAncBytes);
+  };
   auto matrix_phase = [&](int i) __attribute__((always_inline)) {  // P.V of tile i-1, scores of tile i
-    if (i >= 1) mfma_pv(stage_of(i - 1));
+    if (i >= 1 && i - 1 < n_tiles) mfma_pv(stage_of(i - 1));
     __builtin_amdgcn_sched_barrier(0);  // keep the two MFMA chains' operand reads apart
     if (i < n_tiles) {
-      int kind, base;
-      tile_kind(i, kind, base);
-      if (kind == 1) vis_tree = anc_row[base];
       mfma_scores(stage_of(i));
     }
   };
@@ -372,7 +405,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     if (i >= 0 && i < n_tiles) {
       int kind, base;
       tile_kind(i, kind, base);
-      softmax(kind, base);
+      softmax(kind, base, anc_of(i));
     }
   };
   auto compute_phase = [&](int p) __attribute__((always_inline)) {
@@ -393,20 +426,21 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     const TileSrc s1 = tile_src(min(1, n_tiles - 1));
     load_tile(s1, tid, r1s);
     nv1 = s1.nvalid;
-    store_tile(stage_of(0), tid, r0s, nv0);
+    store_tile(stage_of(0), anc_of(0), tid, r0s, nv0);
     const TileSrc s2 = tile_src(min(2, n_tiles - 1));
     load_tile(s2, tid, r0s);
     nv0 = s2.nvalid;
     __syncthreads();
-    // phases 4k .. 4k+3 cover tiles i = 2k (phases 4k, 4k+1) and 2k+1
-    for (int k = 0; 4 * k <= 2 * n_tiles + 1; ++k) {
+    // phases 4k .. 4k+3 cover tiles i = 2k (phases 4k, 4k+1) and 2k+1.  Every
+    // iteration has the same memory operations in the same order (loads past the
+    // last tile re-read it), so the waits before each LDS write cover only the
+    // older register set; phases past the last one compute nothing.
+    const int n_iter = (2 * n_tiles + 2 + 3) / 4;
+    for (int k = 0; k < n_iter; ++k) {
       const int i0 = 2 * k, i1 = 2 * k + 1;
-      // phase 4k (= 2*i0): write tile i0+1 (set 1)
-      if (i0 + 1 < n_tiles) store_tile(stage_of(i0 + 1), tid, r1s, nv1);
+      if (i0 + 1 < n_tiles) store_tile(stage_of(i0 + 1), anc_of(i0 + 1), tid, r1s, nv1);
       compute_phase(4 * k);
       __syncthreads();
-      if (4 * k + 1 > 2 * n_tiles + 1) break;
-      // phase 4k+1: loads of tile i0+3 into set 1
       {
         const TileSrc sn = tile_src(min(i0 + 3, n_tiles - 1));
         load_tile(sn, tid, r1s);
@@ -414,13 +448,9 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
       }
       compute_phase(4 * k + 1);
       __syncthreads();
-      if (4 * k + 2 > 2 * n_tiles + 1) break;
-      // phase 4k+2 (= 2*i1): write tile i1+1 (set 0)
-      if (i1 + 1 < n_tiles) store_tile(stage_of(i1 + 1), tid, r0s, nv0);
+      if (i1 + 1 < n_tiles) store_tile(stage_of(i1 + 1), anc_of(i1 + 1), tid, r0s, nv0);
       compute_phase(4 * k + 2);
       __syncthreads();
-      if (4 * k + 3 > 2 * n_tiles + 1) break;
-      // phase 4k+3: loads of tile i1+3 into set 0
       {
         const TileSrc sn = tile_src(min(i1 + 3, n_tiles - 1));
         load_tile(sn, tid, r0s);
