@@ -122,7 +122,7 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws_a = tv.tree_verify_attention_workspace_size(batch, total, mn, case.max_prefix, case.hq,
                                                    case.hkv, case.d, dt)
-    ws_attn = torch.empty(max(ws_a, 1), dtype=torch.uint8, device="cuda")
+    ws_attn = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device="cuda")
     ws_acc = torch.empty(max(tv.tree_accept_workspace_size(batch, case.vocab), 1), dtype=torch.uint8,
                          device="cuda")
     acc_out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device="cuda"),

@@ -205,7 +205,7 @@ def tree_verify_attention(q, k_cache, v_cache, block_table, prefix_len, k_tree, 
         lse = torch.empty((total, hq), dtype=torch.float32, device=q.device)
     need = tree_verify_attention_workspace_size(batch, total, max_nodes, max_prefix, hq, hkv, d, dt)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zeroed once, kept zero
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     err = _err_word(err, q.device)
     _check("tree_verify_attention",

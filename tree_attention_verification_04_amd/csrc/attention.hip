@@ -1,12 +1,11 @@
-// tree_verify_attention: argument checks, launch plan, split-KV combine.
+// tree_verify_attention: argument checks and launch plan.
 //
 // The plan picks the kernel (matrix-core for bf16 head_dim 128, vector ALU
 // otherwise) and, for the matrix-core kernel, how many workgroups share one
 // (sequence, KV head) prefix.  When one row tile per KV head cannot fill the
 // 256 compute units (a single short verify), the prefix blocks are split over
-// several workgroups and their partial results merged by log-sum-exp:
-//   lse = log sum_i exp(lse_i),  out = sum_i exp(lse_i - lse) * out_i,
-// the same rescaling the online softmax applies between tiles (page
+// several workgroups and a second kernel merges the partial results by
+// log-sum-exp, the same rescaling the online softmax applies between tiles (page
 // "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
 // (ufo.work/2026/537), appendix B).
 #include <algorithm>
@@ -29,8 +28,10 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   const int nblk = ceil_div(std::max(0, max_prefix), 64);
   p.row_tiles = std::max(1, ceil_div(group * max_nodes, kMfmaRowsPerWG));
   const long base = static_cast<long>(batch) * hkv * p.row_tiles;
-  if (nblk > 1 && base < 2 * kCUs) {
-    const int want = std::min(nblk, ceil_div(2 * kCUs, static_cast<int>(base)));
+  // one 512-thread workgroup fits a compute unit (LDS): split the prefix so that a
+  // short verify still spreads over the CUs, without a second round of workgroups
+  if (nblk > 1 && 2 * base <= kCUs) {
+    const int want = std::min<long>(std::min(nblk, kMaxSplits), kCUs / base);
     p.blocks_per_split = ceil_div(nblk, want);
     p.splits = ceil_div(nblk, p.blocks_per_split);
   } else {
@@ -45,37 +46,6 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
     p.workspace = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
   }
   return p;
-}
-
-// One wavefront per (node, head) row merges the split partials.
-__global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long row = static_cast<long>(blockIdx.x) * 4 + wave;
-  if (row >= a.total_rows) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_lse[s * static_cast<long>(a.total_rows) + row]);
-  float w_sum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = a.part_lse[s * static_cast<long>(a.total_rows) + row];
-      const float w = expf(ls - mx);
-      const float2 o = *reinterpret_cast<const float2*>(
-          a.part_o + (s * static_cast<long>(a.total_rows) + row) * 128 + 2 * lane);
-      w_sum += w;
-      o0 = fmaf(w, o.x, o0);
-      o1 = fmaf(w, o.y, o1);
-    }
-  }
-  const float inv = w_sum > 0.0f ? 1.0f / w_sum : 0.0f;
-  uint16_t* out = static_cast<uint16_t*>(a.out) + row * 128 + 2 * lane;
-  out[0] = f32_to_bf16(o0 * inv);
-  out[1] = f32_to_bf16(o1 * inv);
-  if (a.lse != nullptr && lane == 0) a.lse[row] = w_sum > 0.0f ? mx + logf(w_sum) : -INFINITY;
-}
-
-int launch_attn_combine(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_combine, dim3(ceil_div(a.total_rows, 4)), dim3(256), 0, s, a);
-  return check_launch("tree_verify_attention/combine");
 }
 
 }  // namespace tv
@@ -165,12 +135,10 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
     const size_t rows = static_cast<size_t>(total_nodes) * hq;
     const size_t o_bytes = static_cast<size_t>(plan.splits) * rows * head_dim * sizeof(float);
     a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          ((o_bytes + 255) & ~static_cast<size_t>(255)));
+    const size_t o_pad = (o_bytes + 255) & ~static_cast<size_t>(255);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_pad);
   }
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
-  int st = tv::launch_attn_mfma(a, s);
-  if (st != TV_OK || plan.splits == 1) return st;
-  return tv::launch_attn_combine(a, s);
+  return tv::launch_attn_mfma(a, s);
 }

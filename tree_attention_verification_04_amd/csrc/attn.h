@@ -42,9 +42,9 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
 
 int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
-int launch_attn_combine(const AttnArgs& a, hipStream_t s);
 
 constexpr int kMfmaRowsPerWG = 256;  // 8 waves x 32 rows
 constexpr int kCUs = 256;
+constexpr int kMaxSplits = 16;       // prefix splits per (sequence, KV head, row tile)
 
 }  // namespace tv

@@ -461,12 +461,12 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     }
   }
 
-  if (!row_ok) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_tot > 0.0f ? m_run * a.scale + logf(l_tot) : -INFINITY;
   // register v of d-tile dt holds d = 32dt + 8(v/4) + 4*half + v%4
   if (a.splits == 1) {
+    if (!row_ok) return;
     uint16_t* out = static_cast<uint16_t*>(a.out) + grow * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -478,19 +478,62 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
         *reinterpret_cast<uint2*>(out + d) = w;
       }
     if (a.lse != nullptr && half == 0) a.lse[grow] = lse;
-  } else {
-    float* po = a.part_o + (static_cast<long>(split) * a.total_rows + grow) * kD;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d = 32 * dt + 8 * qd + 4 * half;
-        *reinterpret_cast<float4*>(po + d) =
-            make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv,
-                        acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv);
-      }
-    if (half == 0) a.part_lse[static_cast<long>(split) * a.total_rows + grow] = lse;
+    return;
   }
+
+  // ---- split prefix: write this split's normalised partial and its log-sum-exp;
+  // k_attn_combine merges the splits after the kernel ends
+  if (!row_ok) return;
+  float* po = a.part_o + (static_cast<long>(split) * a.total_rows + grow) * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d = 32 * dt + 8 * qd + 4 * half;
+      *reinterpret_cast<float4*>(po + d) =
+          make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv, acc[dt][4 * qd + 2] * inv,
+                      acc[dt][4 * qd + 3] * inv);
+    }
+  if (half == 0) a.part_lse[static_cast<long>(split) * a.total_rows + grow] = lse;
+}
+
+// Merge of the prefix splits, one thread per (row, 4 consecutive d):
+//   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * out_s
+// All splits' values are loaded before any is used (one memory round trip).
+__global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long>(a.total_rows) * (kD / 4)) return;
+  const long gr = idx / (kD / 4);
+  const int d4 = static_cast<int>(idx % (kD / 4));
+  float ls[kMaxSplits];
+  float4 ps[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const bool on = sp < a.splits;
+    const long at = static_cast<long>(on ? sp : 0) * a.total_rows + gr;
+    ls[sp] = a.part_lse[at];
+    ps[sp] = *reinterpret_cast<const float4*>(a.part_o + at * kD + 4 * d4);
+    if (!on) ls[sp] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) mx = fmaxf(mx, ls[sp]);
+  const float mref = mx == -INFINITY ? 0.0f : mx;
+  float w_sum = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const float w = __builtin_amdgcn_exp2f((ls[sp] - mref) * kLog2e);
+    w_sum += w;
+    o.x = fmaf(w, ps[sp].x, o.x);
+    o.y = fmaf(w, ps[sp].y, o.y);
+    o.z = fmaf(w, ps[sp].z, o.z);
+    o.w = fmaf(w, ps[sp].w, o.w);
+  }
+  const float wi = w_sum > 0.0f ? 1.0f / w_sum : 0.0f;
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + gr * kD + 4 * d4) =
+      make_uint2(pack2_bf16(o.x * wi, o.y * wi), pack2_bf16(o.z * wi, o.w * wi));
+  if (a.lse != nullptr && d4 == 0) a.lse[gr] = w_sum > 0.0f ? mx + logf(w_sum) : -INFINITY;
 }
 
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
@@ -502,7 +545,11 @@ int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   }
   const int grid = 8 * ceil_div(a.total_work, 8);
   hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
-  return check_launch("tree_verify_attention/mfma");
+  const int st = check_launch("tree_verify_attention/mfma");
+  if (st != TV_OK || a.splits == 1) return st;
+  const long items = static_cast<long>(a.total_rows) * (kD / 4);
+  hipLaunchKernelGGL(k_attn_combine, dim3(static_cast<int>((items + 255) / 256)), dim3(256), 0, s, a);
+  return check_launch("tree_verify_attention/combine");
 }
 
 }  // namespace tv
