@@ -55,6 +55,77 @@ def attention_cost(case):
     return bytes_, flops
 
 
+ATTN_SOURCES = ("attn_mfma.hip", "attn_vec.hip", "attention.hip", "attn.h")
+COPY_BYTES = 512 << 20  # calibration kernel: reads 512 MiB and writes 512 MiB
+
+
+def attention_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "tree_attention_verification_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(config: int) -> str:
+    return os.path.join(ROOT, "profiles", f"attention_traffic_workload{config}.txt")
+
+
+def recorded_traffic(config: int):
+    """HBM bytes per attention launch from the committed counter summary, if the
+    kernel sources still match the ones the counters were taken with."""
+    try:
+        kv = dict(line.split("=", 1) for line in open(traffic_path(config)).read().split("\n")
+                  if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != attention_source_hash():
+        return None
+    return int(kv["hbm_bytes_per_launch"])
+
+
+def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> None:
+    """Turn FETCH_SIZE / WRITE_SIZE passes into bytes per attention launch.
+
+    Each counter (KiB per dispatch) is scaled by what it reads for a plain
+    elementwise kernel that reads and writes COPY_BYTES (torch.add, same run)."""
+    import csv
+
+    def per_kernel(path):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    def pick(vals, key):
+        rows = [v for k, v in vals.items() if key in k]
+        return sum(rows[0]) / len(rows[0]) if rows else None
+
+    f, w = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy_f = max((sum(v) / len(v) for k, v in f.items() if "add" in k.lower() and "elementwise" in k), default=None)
+    copy_w = max((sum(v) / len(v) for k, v in w.items() if "add" in k.lower() and "elementwise" in k), default=None)
+    sf = COPY_BYTES / (copy_f * 1024.0)
+    sw = COPY_BYTES / (copy_w * 1024.0)
+    attn_f = pick(f, "k_attn_mfma") or pick(f, "k_attn_vec")
+    attn_w = pick(w, "k_attn_mfma") or pick(w, "k_attn_vec")
+    comb_f = pick(f, "k_attn_combine") or 0.0
+    comb_w = pick(w, "k_attn_combine") or 0.0
+    fetch = (attn_f + comb_f) * 1024.0 * sf
+    write = (attn_w + comb_w) * 1024.0 * sw
+    with open(traffic_path(config), "w") as fh:
+        fh.write(f"# HBM traffic of one tree_verify_attention launch, workload {config}\n")
+        fh.write(f"# command: {command}\n")
+        fh.write(f"# FETCH_SIZE KiB/dispatch: attention {attn_f:.1f} combine {comb_f:.1f} copy {copy_f:.1f}\n")
+        fh.write(f"# WRITE_SIZE KiB/dispatch: attention {attn_w:.1f} combine {comb_w:.1f} copy {copy_w:.1f}\n")
+        fh.write(f"# scale factors (copy of {COPY_BYTES} B): fetch {sf:.4f} write {sw:.4f}\n")
+        fh.write(f"fetch_bytes_per_launch={int(fetch)}\n")
+        fh.write(f"write_bytes_per_launch={int(write)}\n")
+        fh.write(f"hbm_bytes_per_launch={int(fetch + write)}\n")
+        fh.write(f"source_hash={attention_source_hash()}\n")
+    print(open(traffic_path(config)).read())
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -98,7 +169,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain copy of a known size first (for counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write the traffic summary for --config from two counter passes")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.config, *args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
@@ -109,6 +187,13 @@ def main():
 
     tv.load()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
     case = W.make_config(args.config, args.seed)
     dev = W.case_to_device(case, "cuda:0")
     mn = max(1, case.max_nodes)
@@ -215,6 +300,7 @@ def main():
         ach = flops / (attn_us * 1e-6) / 1e12
         roof = dict(bound=cbound, achieved=round(ach, 2), peak=cpeak, unit="TFLOP/s",
                     frac=round(ach / cpeak, 4), traffic=None)
+    roof["traffic"] = recorded_traffic(args.config)
     roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
                 alg_bytes=int(bytes_), alg_flops=float(flops))
 
