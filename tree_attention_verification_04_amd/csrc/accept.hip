@@ -9,7 +9,8 @@
 // 机制" (ufo.work/2026/525), §1.2) from norm(max(0, p_target - p_draft)), falling back
 // to p_target itself when that has no mass (same page, §7.2).
 //
-// Three kernels on the caller's stream:
+// Up to 65536 vocabulary entries one kernel does everything (the walk's workgroup
+// scans the rejection row); for larger vocabularies three kernels on the stream:
 //   k_accept_walk    one workgroup per sequence: ratio tests, ancestor walks, the
 //                    deepest accepted node (ties: smallest index), the path, and the
 //                    rejection node c (smallest-index child of the winner).
@@ -28,6 +29,7 @@ namespace tv {
 constexpr int kAcceptThreads = 256;
 constexpr int kResidChunk = 4096;                       // vocabulary entries per chunk
 constexpr int kResidPerThread = kResidChunk / kAcceptThreads;
+constexpr int kFusedVocab = 65536;  // up to this vocabulary the walk's workgroup resamples
 
 #pragma clang fp contract(off)
 
@@ -102,6 +104,49 @@ __device__ uint64_t block_sum_u64(uint64_t v) {
   return all;
 }
 
+// Residual resample of row c inside one workgroup (small vocabularies): thread t
+// sums the integer weights of its contiguous slice, a block scan over the slices
+// finds the one where the running sum passes the threshold, and that thread walks
+// its slice again.  Same integers as the multi-workgroup path, so the same token.
+__device__ void resample_in_block(const float* __restrict__ pt_row, const float* __restrict__ pd_row,
+                                  int vocab, float u, int32_t* __restrict__ out_token,
+                                  int32_t* __restrict__ err) {
+  const int tid = threadIdx.x;
+  const int len = ((vocab + kAcceptThreads - 1) / kAcceptThreads + 3) & ~3;
+  const int k0 = min(vocab, tid * len), k1 = min(vocab, k0 + len);
+  uint64_t sr = 0, st = 0;
+  for (int k = k0; k < k1; ++k) {
+    const float t = pt_row[k];
+    sr += resid_weight(t, pd_row[k]);
+    st += target_weight(t);
+  }
+  const uint64_t zr = block_sum_u64(sr);
+  const uint64_t zt = block_sum_u64(st);
+  const int mode = zr > 0 ? 0 : (zt > 0 ? 1 : -1);
+  if (mode < 0) {
+    if (tid == 0) {
+      *out_token = -1;
+      atomicOr(err, TV_ERR_ZERO_MASS);
+    }
+    return;
+  }
+  const uint64_t t_thr = exact_threshold(u, mode == 0 ? zr : zt);
+  const uint64_t local = mode == 0 ? sr : st;
+  uint64_t total;
+  const uint64_t excl = block_exclusive_scan(local, &total);
+  if (local > 0 && excl <= t_thr && t_thr < excl + local) {
+    uint64_t run = excl;
+    for (int k = k0; k < k1; ++k) {
+      run += mode == 0 ? resid_weight(pt_row[k], pd_row[k]) : target_weight(pt_row[k]);
+      if (run > t_thr) {
+        *out_token = k;
+        break;
+      }
+    }
+  }
+}
+
+template <bool kFused>
 __global__ void __launch_bounds__(kAcceptThreads) k_accept_walk(
     const float* __restrict__ pt, const float* __restrict__ pd, const int32_t* __restrict__ token,
     const float* __restrict__ u_acc, const float* __restrict__ u_res,
@@ -111,7 +156,7 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept_walk(
     uint8_t* __restrict__ node_ok, int32_t* __restrict__ ws_c, int32_t* __restrict__ err) {
   __shared__ int16_t s_par[TV_MAX_NODES];
   __shared__ uint8_t s_acc[TV_MAX_NODES];
-  __shared__ int s_bad, s_key, s_child, s_err;
+  __shared__ int s_bad, s_key, s_child, s_err, s_pending;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int n0 = cu_nodes[b];
   const int n = cu_nodes[b + 1] - n0;
@@ -216,8 +261,16 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept_walk(
       else e |= TV_ERR_UNIFORM;
     }
     ws_c[b] = pending;
+    s_pending = pending;
     if (pending < 0) resample_token[b] = -1;
     if (e) atomicOr(err, e);
+  }
+  if constexpr (kFused) {
+    __syncthreads();
+    const int c = s_pending;
+    if (c < 0) return;
+    const long row = static_cast<long>(n0 + c) * vocab;
+    resample_in_block(pt + row, pd + row, vocab, u_res[n0 + c], resample_token + b, err);
   }
 }
 
@@ -345,9 +398,17 @@ extern "C" int tree_accept(const float* p_target, const float* p_draft, const in
   int32_t* ws_c = static_cast<int32_t*>(workspace);
   const size_t head = (static_cast<size_t>(batch) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
   uint64_t* part = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + head);
-  hipLaunchKernelGGL(tv::k_accept_walk, dim3(batch), dim3(tv::kAcceptThreads), 0, s, p_target,
-                     p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes, vocab,
-                     max_path, accept_len, path, resample_node, resample_token, node_ok, ws_c, err);
+  if (vocab <= tv::kFusedVocab) {  // one kernel: the walk's workgroup also resamples
+    hipLaunchKernelGGL(tv::k_accept_walk<true>, dim3(batch), dim3(tv::kAcceptThreads), 0, s,
+                       p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes,
+                       vocab, max_path, accept_len, path, resample_node, resample_token, node_ok,
+                       ws_c, err);
+    return tv::check_launch("tree_accept/walk");
+  }
+  hipLaunchKernelGGL(tv::k_accept_walk<false>, dim3(batch), dim3(tv::kAcceptThreads), 0, s,
+                     p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes,
+                     vocab, max_path, accept_len, path, resample_node, resample_token, node_ok,
+                     ws_c, err);
   int st = tv::check_launch("tree_accept/walk");
   if (st != TV_OK) return st;
   hipLaunchKernelGGL(tv::k_resid_partial, dim3(chunks, batch), dim3(tv::kAcceptThreads), 0, s,
