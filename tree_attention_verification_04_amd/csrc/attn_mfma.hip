@@ -166,14 +166,20 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   const bool do_tree = split == a.splits - 1;
 
   // ---- this lane's row and its Q fragment (B operand of S^T = K Q^T); issued early
+  // Waves map to (row group rg, key group kg): with R live 32-row groups in this
+  // tile, wave w takes rows rg = w % R and key group kg = w / R.  The pipelined
+  // path uses key group 0 only; short work items spread their tiles over the key
+  // groups and merge the partial softmax states at the end.
   const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int r = r0 + wave * 32 + col;
+  const int n_rg = min(kWaves, (rows - r0 + 31) / 32);
+  const int rg = wave % n_rg, kg = wave / n_rg;
+  const int r = r0 + rg * 32 + col;
   const bool row_ok = r < rows;
   const int node = row_ok ? r / a.group : 0;
   const int head = g * a.group + (row_ok ? r % a.group : 0);
   const long grow = static_cast<long>(n0 + node) * a.hq + head;  // global row (node, head)
-  const bool wave_live = r0 + wave * 32 < rows;
+  bool wave_live = kg == 0;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + grow * kD + half * 8;
   bf16x8_t qf[8];
 #pragma unroll
@@ -331,7 +337,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     const bool full = kind == 0 && plen - base >= kKT;
     if (!full) {
       const uint64_t vis = kind == 0 ? ((1ull << (plen - base)) - 1ull)
-                                     : (row_ok ? anc_slot[wave * 32 + col] : 0ull);
+                                     : (row_ok ? anc_slot[rg * 32 + col] : 0ull);
       // the 32 keys this lane holds, compressed so that register (sg, v) is bit 16sg + v
       const uint32_t lo = static_cast<uint32_t>(vis), hi = static_cast<uint32_t>(vis >> 32);
       const int sh = 8 * half;
@@ -419,7 +425,64 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     }
   };
 
-  if (n_tiles > 0) {
+  if (n_tiles > 0 && n_tiles <= 3) {
+    // Short work items (a split of a short verify): all tiles fit the three
+    // stages, so they are staged once and every live wave runs them back to back
+    // with no further barrier.
+    TileRegs r2s;  // all three tiles in flight at once: one memory round trip
+    const TileSrc s0 = tile_src(0);
+    const TileSrc s1 = tile_src(min(1, n_tiles - 1));
+    const TileSrc s2 = tile_src(min(2, n_tiles - 1));
+    load_tile(s0, tid, r0s);
+    load_tile(s1, tid, r1s);
+    load_tile(s2, tid, r2s);
+    store_tile(stage_of(0), anc_of(0), tid, r0s, s0.nvalid);
+    if (n_tiles > 1) store_tile(stage_of(1), anc_of(1), tid, r1s, s1.nvalid);
+    if (n_tiles > 2) store_tile(stage_of(2), anc_of(2), tid, r2s, s2.nvalid);
+    __syncthreads();
+    const int n_kg = min(kWaves / n_rg, n_tiles);  // key groups that get a tile
+    if (kg < n_kg) {
+      for (int i = kg; i < n_tiles; i += n_kg) {
+        int kind, base;
+        tile_kind(i, kind, base);
+        mfma_scores(stage_of(i));
+        softmax(kind, base, anc_of(i));
+        mfma_pv(stage_of(i));
+      }
+    }
+    if (n_kg > 1) {
+      // merge key groups 1.. into key group 0 through LDS (the stages are free now):
+      //   m = max_k m_k,  l = sum_k l_k e^{m_k - m},  acc = sum_k acc_k e^{m_k - m}
+      __syncthreads();
+      float* slot = reinterpret_cast<float*>(smem) + ((kg - 1) * n_rg + rg) * (66 * 64);
+      if (kg >= 1 && kg < n_kg) {
+        slot[lane] = m_run;
+        slot[64 + lane] = l_run;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) slot[128 + (dt * 16 + v) * 64 + lane] = acc[dt][v];
+      }
+      __syncthreads();
+      if (kg == 0) {
+        for (int k = 1; k < n_kg; ++k) {
+          const float* o = reinterpret_cast<const float*>(smem) + ((k - 1) * n_rg + rg) * (66 * 64);
+          const float mk = o[lane], lk = o[64 + lane];
+          const float m_new = fmaxf(m_run, mk);
+          const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+          const float a0 = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
+          const float a1 = __builtin_amdgcn_exp2f((mk - m_use) * c2);
+          l_run = l_run * a0 + lk * a1;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              acc[dt][v] = acc[dt][v] * a0 + o[128 + (dt * 16 + v) * 64 + lane] * a1;
+          m_run = m_new;
+        }
+      }
+    }
+  } else if (n_tiles > 3) {
     const TileSrc s0 = tile_src(0);
     load_tile(s0, tid, r0s);
     nv0 = s0.nvalid;
@@ -465,6 +528,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse = l_tot > 0.0f ? m_run * a.scale + logf(l_tot) : -INFINITY;
   // register v of d-tile dt holds d = 32dt + 8(v/4) + 4*half + v%4
+  if (kg != 0) return;  // other key groups were merged into key group 0
   if (a.splits == 1) {
     if (!row_ok) return;
     uint16_t* out = static_cast<uint16_t*>(a.out) + grow * kD;
