@@ -55,7 +55,8 @@ def attention_cost(case):
     return bytes_, flops
 
 
-ATTN_SOURCES = ("attn_mfma.hip", "attn_vec.hip", "attention.hip", "attn.h")
+ATTN_SOURCES = ("attn_mfma.hip", "attn_mfma_long.hip", "mfma_tile.h", "attn_vec.hip",
+                "attention.hip", "attn.h")
 COPY_BYTES = 512 << 20  # calibration kernel: reads 512 MiB and writes 512 MiB
 
 

@@ -106,6 +106,14 @@ SMALL = {
     "bf16_d64": ([W.tree_random(np.random.default_rng(8), 70, 6)], [150], 4, 2, 64, W.DT_BF16),
     "fp32_d64_batch": ([W.tree_heap(15), W.tree_star(3), np.zeros(0, np.int32)], [1, 64, 5], 6, 3,
                        64, W.DT_F32),
+    # long work items (64-rows-per-wavefront kernel): many prefix blocks per split,
+    # a last row tile holding a single 32-row group, sequences with no prefix tile in
+    # most splits
+    "long_split_gqa": ([W.tree_random(np.random.default_rng(9), 200, 8)], [8000], 8, 2, 128,
+                       W.DT_BF16),
+    "long_ragged_mha": ([W.tree_random(np.random.default_rng(10), 130, 5), W.tree_chain(5),
+                         W.tree_random(np.random.default_rng(11), 600, 12)], [1000, 37, 513], 4, 4,
+                        128, W.DT_BF16),
 }
 
 

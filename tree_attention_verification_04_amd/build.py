@@ -24,6 +24,8 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # no packed fp32 instructions in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax reads the scores without AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -39,6 +39,7 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
     p.splits = 1;
   }
   p.total_work = base * p.splits;
+  p.long_items = p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(total_nodes) * hq;
     const size_t o_bytes = static_cast<size_t>(p.splits) * rows * head_dim * sizeof(float);
@@ -92,6 +93,8 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
     return tv::fail(TV_EINVAL, "tree_verify_attention: null q, tree K/V, anc_bits, out or prefix_len");
   if (max_prefix > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
     return tv::fail(TV_EINVAL, "tree_verify_attention: null paged cache or block table");
+  if (max_prefix > 0 && num_blocks < 1)
+    return tv::fail(TV_EINVAL, "tree_verify_attention: max_prefix > 0 needs num_blocks >= 1");
   if (static_cast<long>(max_blocks) * 64 < max_prefix)
     return tv::fail(TV_EINVAL, "tree_verify_attention: max_prefix exceeds max_blocks * 64");
   if (static_cast<long>(total_nodes) * hq > INT32_MAX)
@@ -140,5 +143,6 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
   }
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
-  return tv::launch_attn_mfma(a, s);
+  return plan.long_items ? tv::launch_attn_long(a, tv::kLongRowsPerWave, s)
+                         : tv::launch_attn_mfma(a, s);
 }
