@@ -143,6 +143,5 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
   }
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
-  return plan.long_items ? tv::launch_attn_long(a, tv::kLongRowsPerWave, s)
-                         : tv::launch_attn_mfma(a, s);
+  return plan.long_items ? tv::launch_attn_long(a, s) : tv::launch_attn_mfma(a, s);
 }

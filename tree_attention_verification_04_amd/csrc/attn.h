@@ -43,21 +43,16 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
 
 int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
-int launch_attn_long(const AttnArgs& a, int rows_per_wave, hipStream_t s);
+int launch_attn_long(const AttnArgs& a, hipStream_t s);
 int launch_attn_combine(const AttnArgs& a, hipStream_t s);
 
 constexpr int kMfmaRowsPerWG = 256;  // 8 waves x 32 rows
 constexpr int kCUs = 256;
 constexpr int kMaxSplits = 16;       // prefix splits per (sequence, KV head, row tile)
-// work items of at least this many 64-key tiles run the pipelined kernel, with this
-// many rows per wavefront (32: two wavefronts per SIMD; 64: one)
+// work items of at least this many 64-key tiles run the pipelined kernel
 #ifndef TV_LONG_MIN_TILES
 #define TV_LONG_MIN_TILES 8
 #endif
-#ifndef TV_LONG_ROWS_PER_WAVE
-#define TV_LONG_ROWS_PER_WAVE 32
-#endif
 constexpr int kLongMinTiles = TV_LONG_MIN_TILES;
-constexpr int kLongRowsPerWave = TV_LONG_ROWS_PER_WAVE;
 
 }  // namespace tv
