@@ -82,9 +82,11 @@ def test_attention_host_checks(lib):
     assert attn_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
                      ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
     assert b"workspace" in lib.tree_last_error()
-    # the fp32 path and wide batches need no workspace
+    # the fp32 path needs no workspace; one long work item per (sequence, KV head) needs
+    # none either; more long items than compute units need the pair order only
     assert lib.tree_verify_attention_workspace_size(1, 15, 15, 128, 4, 4, 64, tv.TV_DTYPE_F32) == 0
-    assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128, tv.TV_DTYPE_BF16) == 0
+    assert lib.tree_verify_attention_workspace_size(4, 1024, 256, 32768, 64, 8, 128, tv.TV_DTYPE_BF16) == 0
+    assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128, tv.TV_DTYPE_BF16) == 8 * 8 * 4
 
 
 def test_accept_host_checks(lib):

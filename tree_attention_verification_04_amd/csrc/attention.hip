@@ -40,12 +40,22 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   }
   p.total_work = base * p.splits;
   p.long_items = p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
+  // more long work items than compute units, from sequences of different lengths:
+  // rank the (sequence, KV head) pairs by cost and start the longest first
+  const long pairs = static_cast<long>(batch) * hkv;
+  p.ordered = p.long_items && batch > 1 && p.total_work > kCUs && pairs <= kMaxOrderedPairs;
+  size_t ws = 0;
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(total_nodes) * hq;
     const size_t o_bytes = static_cast<size_t>(p.splits) * rows * head_dim * sizeof(float);
     const size_t l_bytes = static_cast<size_t>(p.splits) * rows * sizeof(float);
-    p.workspace = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
+    ws = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
   }
+  if (p.ordered) {
+    p.order_off = (ws + 255) & ~static_cast<size_t>(255);
+    ws = p.order_off + static_cast<size_t>(pairs) * sizeof(int);
+  }
+  p.workspace = ws;
   return p;
 }
 
@@ -143,5 +153,11 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
   }
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
+  if (plan.ordered) {
+    int* order = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.order_off);
+    const int st = tv::launch_attn_order(a, order, s);
+    if (st != TV_OK) return st;
+    a.pair_order = order;
+  }
   return plan.long_items ? tv::launch_attn_long(a, s) : tv::launch_attn_mfma(a, s);
 }

@@ -21,6 +21,7 @@ struct AttnArgs {
   float* part_o;            // [splits, total_rows, D] fp32 (split-KV partials)
   float* part_lse;          // [splits, total_rows]
   int32_t* err;
+  const int* pair_order;    // [batch * hkv] (sequence, KV head) pairs, longest first; or null
   int words, batch, total_nodes, total_rows, max_nodes, max_prefix;
   int num_blocks, max_blocks, hq, hkv, group;
   int splits, blocks_per_split, row_tiles, total_work;
@@ -31,11 +32,13 @@ struct AttnArgs {
 struct AttnPlan {
   bool mfma;          // bf16, head_dim 128: matrix-core kernel; else the vector kernel
   bool long_items;    // pipelined matrix-core kernel for work items of many tiles
+  bool ordered;       // long items dispatched longest (sequence, KV head) first
   int splits;         // prefix split across workgroups (1 = no combine pass)
   int blocks_per_split;
   int row_tiles;      // row tiles per (sequence, kv head)
   long total_work;    // workgroups with work
-  size_t workspace;   // bytes of split partials
+  size_t workspace;   // bytes of split partials and of the pair order
+  size_t order_off;   // workspace offset of the pair order
 };
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
@@ -44,6 +47,7 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
 int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 int launch_attn_long(const AttnArgs& a, hipStream_t s);
+int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s);
 int launch_attn_combine(const AttnArgs& a, hipStream_t s);
 
 constexpr int kMfmaRowsPerWG = 256;  // 8 waves x 32 rows
@@ -54,5 +58,6 @@ constexpr int kMaxSplits = 16;       // prefix splits per (sequence, KV head, ro
 #define TV_LONG_MIN_TILES 8
 #endif
 constexpr int kLongMinTiles = TV_LONG_MIN_TILES;
+constexpr int kMaxOrderedPairs = 2048;  // pairs the ordering kernel ranks in one workgroup
 
 }  // namespace tv

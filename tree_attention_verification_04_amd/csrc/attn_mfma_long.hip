@@ -120,14 +120,17 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kMaskOff);
 
-  // ---- work item (XCD-aware: consecutive work indices share an XCD)
-  const int per_xcd = gridDim.x / 8;
-  const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (work >= a.total_work) return;
-  const int tile = work % a.row_tiles;
-  const int rest = work / a.row_tiles;
-  const int split = rest % a.splits;
-  const int pair = rest / a.splits;
+  // ---- work item.  Pair rank r (in pair_order, longest first, when given) goes to
+  // XCD r % 8; the m = row_tiles * splits work items of a pair get consecutive
+  // dispatch slots of that XCD, so they run together and share its L2.
+  const int m_items = a.row_tiles * a.splits;
+  const int xcd = blockIdx.x % 8, k_slot = blockIdx.x / 8;
+  const int rank = 8 * (k_slot / m_items) + xcd;
+  if (rank >= a.batch * a.hkv) return;
+  const int pair = a.pair_order != nullptr ? a.pair_order[rank] : rank;
+  const int member = k_slot % m_items;
+  const int tile = member % a.row_tiles;
+  const int split = member / a.row_tiles;
   const int g = pair % a.hkv;
   const int b = pair / a.hkv;
 
@@ -516,11 +519,53 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
     attr_set = true;
   }
-  const int grid = 8 * ceil_div(a.total_work, 8);
+  const int grid = 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
   hipLaunchKernelGGL(k_attn_long, dim3(grid), dim3(kTL), kSmemL, s, a);
   const int st = check_launch("tree_verify_attention/long");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);
+}
+
+// ---- dispatch order of the long work items: the (sequence, KV head) pairs ranked
+// by estimated cost, largest first (longest-processing-time-first list scheduling;
+// the hardware hands each freed compute unit the next workgroup in dispatch order).
+// Cost of a pair = its tiles x its live 64-row units summed over its row tiles, from
+// the same clamped lengths the attention kernel uses.  One workgroup; rank of pair i
+// = number of pairs with a larger cost, or an equal cost and a smaller index.
+__global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
+  __shared__ unsigned long long s_key[kMaxOrderedPairs];
+  const int pairs = a.batch * a.hkv;
+  for (int p = threadIdx.x; p < pairs; p += 1024) {
+    const int b = p / a.hkv;
+    const int n0 = a.cu_nodes[b];
+    const int count = max(0, min(a.cu_nodes[b + 1] - n0, a.max_nodes));
+    const int plen = max(0, min(a.prefix_len[b], min(a.max_prefix, a.max_blocks * 64)));
+    const int tiles = (plen + kKT - 1) / kKT + (count + 63) / 64;
+    const int rows = a.group * count;
+    int units = 0;
+    for (int t = 0; t < a.row_tiles; ++t) {
+      const int live = rows - t * kMfmaRowsPerWG;
+      if (live > 0) units += (min(live, kMfmaRowsPerWG) + 63) / 64;
+    }
+    s_key[p] = (static_cast<unsigned long long>(tiles) * units << 32) | static_cast<unsigned>(p);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < pairs; i += 1024) {
+    const unsigned long long ki = s_key[i];
+    const unsigned ci = static_cast<unsigned>(ki >> 32);
+    int rank = 0;
+    for (int j = 0; j < pairs; ++j) {
+      const unsigned long long kj = s_key[j];
+      const unsigned cj = static_cast<unsigned>(kj >> 32);
+      rank += (cj > ci) || (cj == ci && j < i);
+    }
+    order[rank] = i;
+  }
+}
+
+int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s) {
+  hipLaunchKernelGGL(k_attn_order, dim3(1), dim3(1024), 0, s, a, order);
+  return check_launch("tree_verify_attention/order");
 }
 
 }  // namespace tv
