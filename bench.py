@@ -108,17 +108,20 @@ def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> 
     copy_w = max((sum(v) / len(v) for k, v in w.items() if "add" in k.lower() and "elementwise" in k), default=None)
     sf = COPY_BYTES / (copy_f * 1024.0)
     sw = COPY_BYTES / (copy_w * 1024.0)
-    attn_f = pick(f, "k_attn_mfma") or pick(f, "k_attn_vec")
-    attn_w = pick(w, "k_attn_mfma") or pick(w, "k_attn_vec")
-    comb_f = pick(f, "k_attn_combine") or 0.0
-    comb_w = pick(w, "k_attn_combine") or 0.0
+    # one tree_verify_attention launch: its main kernel plus the split merge and the
+    # pair-order kernel when the plan uses them
+    main_keys = ("k_attn_long", "k_attn_mfma", "k_attn_vec")
+    attn_f = next((v for v in (pick(f, k) for k in main_keys) if v is not None), 0.0)
+    attn_w = next((v for v in (pick(w, k) for k in main_keys) if v is not None), 0.0)
+    comb_f = (pick(f, "k_attn_combine") or 0.0) + (pick(f, "k_attn_order") or 0.0)
+    comb_w = (pick(w, "k_attn_combine") or 0.0) + (pick(w, "k_attn_order") or 0.0)
     fetch = (attn_f + comb_f) * 1024.0 * sf
     write = (attn_w + comb_w) * 1024.0 * sw
     with open(traffic_path(config), "w") as fh:
         fh.write(f"# HBM traffic of one tree_verify_attention launch, workload {config}\n")
         fh.write(f"# command: {command}\n")
-        fh.write(f"# FETCH_SIZE KiB/dispatch: attention {attn_f:.1f} combine {comb_f:.1f} copy {copy_f:.1f}\n")
-        fh.write(f"# WRITE_SIZE KiB/dispatch: attention {attn_w:.1f} combine {comb_w:.1f} copy {copy_w:.1f}\n")
+        fh.write(f"# FETCH_SIZE KiB/dispatch: attention {attn_f:.1f} merge+order {comb_f:.1f} copy {copy_f:.1f}\n")
+        fh.write(f"# WRITE_SIZE KiB/dispatch: attention {attn_w:.1f} merge+order {comb_w:.1f} copy {copy_w:.1f}\n")
         fh.write(f"# scale factors (copy of {COPY_BYTES} B): fetch {sf:.4f} write {sw:.4f}\n")
         fh.write(f"fetch_bytes_per_launch={int(fetch)}\n")
         fh.write(f"write_bytes_per_launch={int(write)}\n")

@@ -550,16 +550,18 @@ __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
     s_key[p] = (static_cast<unsigned long long>(tiles) * units << 32) | static_cast<unsigned>(p);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < pairs; i += 1024) {
-    const unsigned long long ki = s_key[i];
-    const unsigned ci = static_cast<unsigned>(ki >> 32);
+  // one wavefront per pair: its lanes count the larger keys, then sum the counts
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = wave; i < pairs; i += 1024 / 64) {
+    const unsigned ci = static_cast<unsigned>(s_key[i] >> 32);
     int rank = 0;
-    for (int j = 0; j < pairs; ++j) {
-      const unsigned long long kj = s_key[j];
-      const unsigned cj = static_cast<unsigned>(kj >> 32);
+    for (int j = lane; j < pairs; j += 64) {
+      const unsigned cj = static_cast<unsigned>(s_key[j] >> 32);
       rank += (cj > ci) || (cj == ci && j < i);
     }
-    order[rank] = i;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) rank += __shfl_xor(rank, off, 64);
+    if (lane == 0) order[rank] = i;
   }
 }
 
