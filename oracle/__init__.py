@@ -22,9 +22,10 @@ from .tree import (ERR_BAD_PARENT, ERR_TOO_MANY_NODES, ERR_TOKEN, ERR_BLOCK, ERR
                    ERR_PATH, ERR_UNIFORM, ancestors_or_self, depths, anc_bitsets, build_index)
 from .attention import tree_attention
 from .acceptance import accept, accept_sequence, residual_token
+from .commit import commit_kv
 
 __all__ = [
     "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES", "ERR_TOKEN", "ERR_BLOCK", "ERR_ZERO_MASS",
     "ERR_PATH", "ERR_UNIFORM", "ancestors_or_self", "depths", "anc_bitsets", "build_index",
-    "tree_attention", "accept", "accept_sequence", "residual_token",
+    "tree_attention", "accept", "accept_sequence", "residual_token", "commit_kv",
 ]

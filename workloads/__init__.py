@@ -317,12 +317,16 @@ def _normal_tensor(rng: np.random.Generator, shape, dtype: int) -> np.ndarray:
 
 def make_case(name: str, parents: list[np.ndarray], prefix_lens: list[int], hq: int, hkv: int,
               d: int, dtype: int, vocab: int, seed: int, *, alias_prefix: bool = False,
-              with_probs: bool = True, spare_blocks: int = 0, sigma2: float = 2.0) -> Case:
+              with_probs: bool = True, spare_blocks: int = 0, sigma2: float = 2.0,
+              reserve_tokens: int = 0) -> Case:
     """Draw every input of one verify step for the given trees and prefixes.
 
     alias_prefix: all sequences' block tables point at the same physical
     blocks (one shared prefix, read through every sequence's table).
+    reserve_tokens: each sequence's table also maps the blocks of this many
+    positions past its prefix (fresh blocks of the pool, room for a commit).
     """
+    assert not (alias_prefix and reserve_tokens), "a shared prefix has no private room"
     batch = len(parents)
     assert len(prefix_lens) == batch
     cu = np.zeros(batch + 1, dtype=np.int32)
@@ -331,7 +335,7 @@ def make_case(name: str, parents: list[np.ndarray], prefix_lens: list[int], hq: 
     total = int(cu[-1])
     parent = np.concatenate([np.asarray(p, dtype=np.int32) for p in parents]) if total else np.zeros(0, np.int32)
     plen = np.asarray(prefix_lens, dtype=np.int32)
-    nblk = [(int(p) + BLOCK - 1) // BLOCK for p in plen]
+    nblk = [(int(p) + reserve_tokens + BLOCK - 1) // BLOCK for p in plen]
     max_blocks = max([1] + nblk)
     rng_layout = _rng(seed, 11)
     if alias_prefix:
