@@ -130,6 +130,64 @@ def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> 
     print(open(traffic_path(config)).read())
 
 
+def measure_commit(tv, case, dev, acc_out, max_path: int, reps: int) -> dict:
+    """tree_commit_kv after this step's acceptance, timed alone (not part of the step).
+
+    The accepted paths of the step are appended to a fresh paged pool whose block
+    table reserves reps * max_path positions past each prefix; prefix_len is reset
+    before every timed graph replay (outside the timed region).  Algorithmic bytes =
+    accepted rows x hkv x head_dim x element size x 2 (K, V) x 2 (read, write)."""
+    import torch
+    import workloads as W
+    elt = 4 if case.dtype == W.DT_F32 else 2
+    plen = case.prefix_len.astype(np.int64)
+    nblk = (plen + reps * max_path + 63) // 64
+    max_blocks = int(nblk.max())
+    bt = np.full((case.batch, max_blocks), -1, dtype=np.int32)
+    o = 0
+    for b in range(case.batch):
+        bt[b, :nblk[b]] = np.arange(o, o + nblk[b], dtype=np.int32)
+        o += int(nblk[b])
+    tdt = dev["k_tree"].dtype
+    k_pool = torch.zeros((o, case.hkv, 64, case.d), dtype=tdt, device="cuda")
+    v_pool = torch.zeros_like(k_pool)
+    bt_d = torch.from_numpy(bt).cuda()
+    plen0 = dev["prefix_len"].clone()
+    plen_d = plen0.clone()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def commit():
+        tv.tree_commit_kv(dev["k_tree"], dev["v_tree"], dev["cu_nodes"], acc_out["accept_len"],
+                          acc_out["path"], k_pool, v_pool, bt_d, plen_d, err=err)
+
+    commit()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            commit()
+    times = []
+    for _ in range(5):
+        plen_d.copy_(plen0)
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        times.append(s_ev.elapsed_time(e_ev) / reps)
+    if int(err.item()) != 0:
+        raise SystemExit(f"commit: device error word {int(err.item())}")
+    us = float(np.median(times)) * 1e3
+    rows = int(acc_out["accept_len"].sum().item())
+    bytes_ = rows * case.hkv * case.d * elt * 2 * 2
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return dict(us_per_call=round(us, 3), accepted_rows=rows, alg_bytes=bytes_,
+                achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 5), bound="hbm",
+                note="latency-bound: a few KB to MB per call")
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -308,6 +366,8 @@ def main():
     roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
                 alg_bytes=int(bytes_), alg_flops=float(flops))
 
+    commit = measure_commit(tv, case, dev, acc_out, max_path, reps)
+
     res = {
         "metric": "verified tree tokens/s",
         "value": round(total / (ms_step * 1e-3), 1),
@@ -329,6 +389,7 @@ def main():
                    "timing": "HIP-graph replay, events on the launch stream",
                    "wall_s": round(wall, 3)},
         "roofline": roof,
+        "next_rows": {"kv_commit": commit},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

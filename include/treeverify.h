@@ -15,6 +15,8 @@
  *   tree_verify_attention every tree node attends to the shared paged prefix
  *                         and to its own ancestors (mask M_tree)
  *   tree_accept           ratio test, longest accepted path, residual resample
+ * and a fourth that follows it:
+ *   tree_commit_kv        the accepted path's K/V become prefix positions
  *
  * Conventions shared by every call
  *   - Every array pointer is DEVICE memory owned by the caller; the library
@@ -182,6 +184,37 @@ int tree_accept(const float* p_target, const float* p_draft, const int32_t* toke
                 int32_t vocab, int32_t max_path, int32_t* accept_len, int32_t* path,
                 int32_t* resample_node, int32_t* resample_token, uint8_t* node_ok,
                 void* workspace, size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * tree_commit_kv — append each sequence's accepted path to its paged prefix.
+ *
+ * Node path[b][j] (local id, j < accept_len[b]) holds the keys and values of
+ * position prefix_len[b] + j: its rows of every KV head are copied to that
+ * position of the paged cache, and prefix_len[b] grows by accept_len[b], so the
+ * next verify round reads them as shared prefix ([P537] §5.2, prefix caching of
+ * the accepted path; [P525] §2.3.2, the tree's KV slots return to the pool after
+ * verification; [P525] §8.1, accepted length and new KV indices as verify outputs).
+ * The block table must already map the logical blocks of the new positions (the
+ * caller reserves them; nothing is allocated here).
+ *
+ *   k_tree/v_tree   [total_nodes, hkv, head_dim], dtype (must not overlap the cache)
+ *   cu_nodes        [batch + 1] int32
+ *   accept_len      [batch] int32; path [batch, max_path] int32 (tree_accept's outputs)
+ *   k_cache/v_cache [num_blocks, hkv, TV_BLOCK, head_dim], dtype: written
+ *   block_table     [batch, max_blocks] int32
+ *   prefix_len      [batch] int32: read, then increased in place
+ *   head_dim 64 or 128; dtype TV_DTYPE_F32 or TV_DTYPE_BF16
+ *   err             TV_ERR_PATH (accept_len outside [0, max_path], or a path entry
+ *                   outside the sequence's nodes), TV_ERR_BLOCK (a new position beyond
+ *                   the table or mapped to a block outside [0, num_blocks)); such a
+ *                   sequence is left untouched (cache and prefix_len)
+ */
+int tree_commit_kv(const void* k_tree, const void* v_tree, const int32_t* cu_nodes,
+                   const int32_t* accept_len, const int32_t* path, int32_t batch,
+                   int32_t total_nodes, int32_t max_path, int32_t hkv, int32_t head_dim,
+                   int32_t dtype, void* k_cache, void* v_cache, int32_t num_blocks,
+                   const int32_t* block_table, int32_t max_blocks, int32_t* prefix_len,
+                   int32_t* err, void* stream);
 
 /* Reason for the last non-TV_OK status on the calling thread ("" if none). */
 const char* tree_last_error(void);

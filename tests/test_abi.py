@@ -117,3 +117,27 @@ def test_binding_refuses_cpu_tensors(lib):
     cu = torch.tensor([0, 2], dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU tensor"):
         tv.tree_build_index(par, cu, 2)
+
+
+def commit_call(lib, **kw):
+    one = ctypes.c_void_p(16)
+    args = dict(kt=one, vt=one, cu=one, acc=one, path=one, batch=2, total=5, max_path=4, hkv=2,
+                d=128, dtype=tv.TV_DTYPE_BF16, kc=one, vc=one, nblocks=4, bt=one, max_blocks=2,
+                plen=one, err=one, stream=None)
+    args.update(kw)
+    return lib.tree_commit_kv(*args.values())
+
+
+def test_commit_host_checks(lib):
+    assert commit_call(lib, d=96) == tv.TV_EUNSUPPORTED
+    assert commit_call(lib, dtype=5) == tv.TV_EUNSUPPORTED
+    assert commit_call(lib, hkv=0) == tv.TV_EINVAL
+    assert commit_call(lib, batch=-1) == tv.TV_EINVAL
+    assert commit_call(lib, max_path=-2) == tv.TV_EINVAL
+    assert commit_call(lib, err=None) == tv.TV_EINVAL
+    assert commit_call(lib, plen=None) == tv.TV_EINVAL
+    assert commit_call(lib, path=None) == tv.TV_EINVAL
+    assert b"path" in lib.tree_last_error()
+    assert commit_call(lib, kt=None) == tv.TV_EINVAL
+    # nothing to do: no sequences (returns before any launch)
+    assert commit_call(lib, batch=0, kt=None, vt=None, path=None) == tv.TV_OK

@@ -39,6 +39,7 @@ EXPORTS = (
     "tree_verify_attention",
     "tree_accept_workspace_size",
     "tree_accept",
+    "tree_commit_kv",
     "tree_last_error",
 )
 
@@ -64,6 +65,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_accept_workspace_size.restype = Z
     lib.tree_accept.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P, P]
     lib.tree_accept.restype = ctypes.c_int
+    lib.tree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, I, P, I, P, P, P]
+    lib.tree_commit_kv.restype = ctypes.c_int
     lib.tree_last_error.argtypes = []
     lib.tree_last_error.restype = ctypes.c_char_p
 
@@ -262,3 +265,37 @@ def tree_accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes
                            _ptr(o.get("node_ok")), _ptr(workspace),
                            workspace.numel(), _ptr(err), _stream(stream)))
     return o
+
+
+def tree_commit_kv(k_tree, v_tree, cu_nodes, accept_len, path, k_cache, v_cache, block_table,
+                   prefix_len, *, err=None, stream=None) -> torch.Tensor:
+    """Append each sequence's accepted path (tree_accept's accept_len / path) to its
+    paged prefix: K/V rows copied to positions prefix_len[b] + j, prefix_len
+    increased in place.  Returns the error word."""
+    lib = load()
+    _need(k_tree, "k_tree", (torch.float32, torch.bfloat16), 3)
+    _need(v_tree, "v_tree", k_tree.dtype, 3)
+    _need(k_cache, "k_cache", k_tree.dtype, 4)
+    _need(v_cache, "v_cache", k_tree.dtype, 4)
+    for name, t in (("cu_nodes", cu_nodes), ("accept_len", accept_len), ("prefix_len", prefix_len)):
+        _need(t, name, torch.int32, 1)
+    _need(path, "path", torch.int32, 2)
+    _need(block_table, "block_table", torch.int32, 2)
+    total, hkv, d = k_tree.shape
+    if tuple(v_tree.shape) != (total, hkv, d):
+        raise ValueError("v_tree must match k_tree")
+    num_blocks = k_cache.shape[0]
+    if tuple(k_cache.shape[1:]) != (hkv, TV_BLOCK, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks, hkv, 64, head_dim]")
+    batch = cu_nodes.numel() - 1
+    if accept_len.numel() != batch or path.shape[0] != batch or prefix_len.numel() != batch \
+            or block_table.shape[0] != batch:
+        raise ValueError("accept_len, path, prefix_len and block_table need one row per sequence")
+    err = _err_word(err, k_tree.device)
+    _check("tree_commit_kv",
+           lib.tree_commit_kv(_ptr(k_tree), _ptr(v_tree), _ptr(cu_nodes), _ptr(accept_len),
+                              _ptr(path), batch, total, path.shape[1], hkv, d,
+                              dtype_code(k_tree.dtype), _ptr(k_cache), _ptr(v_cache), num_blocks,
+                              _ptr(block_table), block_table.shape[1], _ptr(prefix_len), _ptr(err),
+                              _stream(stream)))
+    return err
