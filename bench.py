@@ -188,6 +188,58 @@ def measure_commit(tv, case, dev, acc_out, max_path: int, reps: int) -> dict:
                 note="latency-bound: a few KB to MB per call")
 
 
+def measure_softmax(tv, case, reps: int) -> dict:
+    """tree_softmax_rows for this workload's trees, timed alone (not part of the step).
+
+    Context rows: the prefix end and every node with a child (a node is judged at its
+    parent's context); logits ~ N(0, 2) per context row.  Algorithmic bytes = logits
+    read once (4 V per context row) + probabilities written (4 V per node)."""
+    import torch
+    row_of, ctx = [], 0
+    for b in range(case.batch):
+        par = case.parent[case.cu_nodes[b]:case.cu_nodes[b + 1]]
+        m = {-1: ctx}
+        ctx += 1
+        for p in par:
+            if p >= 0 and int(p) not in m:
+                m[int(p)] = ctx
+                ctx += 1
+        row_of += [m[int(p)] for p in par]
+    rng = np.random.default_rng(7)
+    lg = torch.from_numpy((rng.standard_normal((ctx, case.vocab)) * np.sqrt(2.0)).astype(np.float32)).cuda()
+    ro = torch.tensor(row_of, dtype=torch.int32, device="cuda")
+    probs = torch.empty((len(row_of), case.vocab), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, int(tv.load().tree_softmax_rows_workspace_size(ctx, case.vocab))),
+                     dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    run = lambda: tv.tree_softmax_rows(lg, ro, probs=probs, workspace=ws, err=err)
+    run()
+    torch.cuda.synchronize()
+    n = max(1, min(reps, int(2e9 // max(1, probs.numel() * 4))))  # bound the graph's traffic
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        times.append(s_ev.elapsed_time(e_ev) / n)
+    if int(err.item()) != 0:
+        raise SystemExit(f"softmax rows: device error word {int(err.item())}")
+    us = float(np.median(times)) * 1e3
+    bytes_ = 4 * case.vocab * (ctx + len(row_of))
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return dict(us_per_call=round(us, 3), context_rows=ctx, rows=len(row_of), vocab=case.vocab,
+                alg_bytes=bytes_, achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm")
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -367,6 +419,7 @@ def main():
                 alg_bytes=int(bytes_), alg_flops=float(flops))
 
     commit = measure_commit(tv, case, dev, acc_out, max_path, reps)
+    softmax = measure_softmax(tv, case, reps)
 
     res = {
         "metric": "verified tree tokens/s",
@@ -389,7 +442,7 @@ def main():
                    "timing": "HIP-graph replay, events on the launch stream",
                    "wall_s": round(wall, 3)},
         "roofline": roof,
-        "next_rows": {"kv_commit": commit},
+        "next_rows": {"kv_commit": commit, "softmax_rows": softmax},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

@@ -66,6 +66,7 @@ extern "C" {
 #define TV_ERR_ZERO_MASS 16      /* residual and target mass both zero at the rejection node */
 #define TV_ERR_PATH 32           /* accepted path longer than max_path */
 #define TV_ERR_UNIFORM 64        /* a uniform outside [0, 1) or NaN */
+#define TV_ERR_ROW 128           /* a context-row index outside [0, ctx_rows) */
 
 /* element types */
 #define TV_DTYPE_F32 0
@@ -215,6 +216,32 @@ int tree_commit_kv(const void* k_tree, const void* v_tree, const int32_t* cu_nod
                    int32_t dtype, void* k_cache, void* v_cache, int32_t num_blocks,
                    const int32_t* block_table, int32_t max_blocks, int32_t* prefix_len,
                    int32_t* err, void* stream);
+
+/*
+ * tree_softmax_rows — probability rows from target logits, before tree_accept.
+ *
+ * One forward pass over the tree gives one logits row per context ([P537] §2.2.3);
+ * a drafted token is judged by the distribution at its parent's context, so
+ * siblings share a row:
+ *   probs[i][k] = exp(t*logits[r][k] - M_r) / sum_k' exp(t*logits[r][k'] - M_r),
+ *   r = row_of[i] (or i when row_of is NULL), M_r = max_k t*logits[r][k]
+ * (the maximum subtracted first: [P525] §7.1, log-sum-exp trick).  Computed in
+ * fp32: relative error of each probability below 5e-6.
+ *
+ *   logits      [ctx_rows, vocab] float
+ *   row_of      [rows] int32 or NULL (then rows == ctx_rows)
+ *   inv_temperature  t > 0 (1 = plain softmax)
+ *   probs       out [rows, vocab] float; a row whose row_of entry is outside
+ *               [0, ctx_rows) is zero-filled and sets TV_ERR_ROW
+ *   workspace   >= tree_softmax_rows_workspace_size(ctx_rows, vocab) bytes; no
+ *               initial contents needed; calls sharing one must not overlap
+ * Two kernels, HBM-bound; rows and vocab / 8192 at most 65535.
+ */
+size_t tree_softmax_rows_workspace_size(int32_t ctx_rows, int32_t vocab);
+
+int tree_softmax_rows(const float* logits, int32_t ctx_rows, int32_t vocab, const int32_t* row_of,
+                      int32_t rows, float inv_temperature, float* probs, void* workspace,
+                      size_t workspace_bytes, int32_t* err, void* stream);
 
 /* Reason for the last non-TV_OK status on the calling thread ("" if none). */
 const char* tree_last_error(void);

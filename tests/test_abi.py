@@ -7,6 +7,7 @@ import re
 import pytest
 
 import tree_attention_verification_04_amd as tv
+import oracle.probs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "treeverify.h")
@@ -141,3 +142,19 @@ def test_commit_host_checks(lib):
     assert commit_call(lib, kt=None) == tv.TV_EINVAL
     # nothing to do: no sequences (returns before any launch)
     assert commit_call(lib, batch=0, kt=None, vt=None, path=None) == tv.TV_OK
+
+
+def test_softmax_rows_host_checks(lib):
+    one = ctypes.c_void_p(16)
+    call = lambda **kw: lib.tree_softmax_rows(*{**dict(lg=one, c=4, v=1000, row_of=None, r=4, t=1.0,
+                                                       p=one, ws=one, wsb=64, err=one, s=None),
+                                               **kw}.values())
+    assert lib.tree_softmax_rows_workspace_size(4, 1000) == 4 * 1 * 8
+    assert lib.tree_softmax_rows_workspace_size(2, 152064) == 2 * 19 * 8
+    assert call(t=0.0) == tv.TV_EINVAL
+    assert call(r=5) == tv.TV_EINVAL                 # rows != ctx_rows without row_of
+    assert call(c=-1) == tv.TV_EINVAL
+    assert call(err=None) == tv.TV_EINVAL
+    assert call(wsb=8) == tv.TV_EWORKSPACE
+    assert call(r=0, c=0) == tv.TV_OK                # nothing to do
+    assert tv.TV_ERR_ROW == oracle.probs.ERR_ROW

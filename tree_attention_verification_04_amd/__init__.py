@@ -29,6 +29,7 @@ TV_ERR_BLOCK = 8
 TV_ERR_ZERO_MASS = 16
 TV_ERR_PATH = 32
 TV_ERR_UNIFORM = 64
+TV_ERR_ROW = 128
 TV_DTYPE_F32, TV_DTYPE_BF16 = 0, 1
 TV_MAX_NODES = 2048
 TV_BLOCK = 64
@@ -40,6 +41,8 @@ EXPORTS = (
     "tree_accept_workspace_size",
     "tree_accept",
     "tree_commit_kv",
+    "tree_softmax_rows_workspace_size",
+    "tree_softmax_rows",
     "tree_last_error",
 )
 
@@ -67,6 +70,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_accept.restype = ctypes.c_int
     lib.tree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, I, P, I, P, P, P]
     lib.tree_commit_kv.restype = ctypes.c_int
+    lib.tree_softmax_rows_workspace_size.argtypes = [I, I]
+    lib.tree_softmax_rows_workspace_size.restype = Z
+    lib.tree_softmax_rows.argtypes = [P, I, I, P, I, F, P, P, Z, P, P]
+    lib.tree_softmax_rows.restype = ctypes.c_int
     lib.tree_last_error.argtypes = []
     lib.tree_last_error.restype = ctypes.c_char_p
 
@@ -299,3 +306,29 @@ def tree_commit_kv(k_tree, v_tree, cu_nodes, accept_len, path, k_cache, v_cache,
                               _ptr(block_table), block_table.shape[1], _ptr(prefix_len), _ptr(err),
                               _stream(stream)))
     return err
+
+
+def tree_softmax_rows(logits, row_of=None, *, inv_temperature: float = 1.0, probs=None,
+                      workspace=None, err=None, stream=None):
+    """Probability rows softmax(t * logits[row_of[i]]) (row_of=None: one row per
+    logits row).  Returns (probs [rows, vocab] float32, err)."""
+    lib = load()
+    _need(logits, "logits", torch.float32, 2)
+    ctx_rows, vocab = logits.shape
+    if row_of is not None:
+        _need(row_of, "row_of", torch.int32, 1)
+    rows = ctx_rows if row_of is None else row_of.numel()
+    if probs is None:
+        probs = torch.empty((rows, vocab), dtype=torch.float32, device=logits.device)
+    _need(probs, "probs", torch.float32, 2)
+    if tuple(probs.shape) != (rows, vocab):
+        raise ValueError("probs must be [rows, vocab]")
+    need = int(lib.tree_softmax_rows_workspace_size(ctx_rows, vocab))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=logits.device)
+    err = _err_word(err, logits.device)
+    _check("tree_softmax_rows",
+           lib.tree_softmax_rows(_ptr(logits), ctx_rows, vocab, _ptr(row_of), rows,
+                                 float(inv_temperature), _ptr(probs), _ptr(workspace),
+                                 workspace.numel(), _ptr(err), _stream(stream)))
+    return probs, err
