@@ -29,10 +29,11 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   p.row_tiles = std::max(1, ceil_div(group * max_nodes, kMfmaRowsPerWG));
   const long base = static_cast<long>(batch) * hkv * p.row_tiles;
   // one 512-thread workgroup fits a compute unit (LDS): split the prefix so that a
-  // short verify still spreads over the CUs, without a second round of workgroups
-  if (nblk > 1 && 2 * base <= kCUs) {
+  // short verify still spreads over the CUs, without a second round of workgroups,
+  // but keep enough blocks per split for the tile pipeline to hide memory latency
+  if (nblk > kMinSplitBlocks && 2 * base <= kCUs) {
     const int want = std::min<long>(std::min(nblk, kMaxSplits), kCUs / base);
-    p.blocks_per_split = ceil_div(nblk, want);
+    p.blocks_per_split = std::max(kMinSplitBlocks, ceil_div(nblk, want));
     p.splits = ceil_div(nblk, p.blocks_per_split);
   } else {
     p.blocks_per_split = std::max(1, nblk);

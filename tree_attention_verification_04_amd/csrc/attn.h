@@ -55,9 +55,10 @@ constexpr int kCUs = 256;
 constexpr int kMaxSplits = 16;       // prefix splits per (sequence, KV head, row tile)
 // work items of at least this many 64-key tiles run the pipelined kernel
 #ifndef TV_LONG_MIN_TILES
-#define TV_LONG_MIN_TILES 8
+#define TV_LONG_MIN_TILES 4
 #endif
 constexpr int kLongMinTiles = TV_LONG_MIN_TILES;
+constexpr int kMinSplitBlocks = 4;   // prefix blocks per split at least (when splitting)
 constexpr int kMaxOrderedPairs = 2048;  // pairs the ordering kernel ranks in one workgroup
 
 }  // namespace tv
