@@ -28,6 +28,40 @@ struct AttnArgs {
   float scale;              // softmax scale (natural-exp units)
 };
 
+// Kernel arguments sit in memory, and each first use of a field would otherwise
+// wait for its own scalar load; naming them all at entry requests them together,
+// one memory round trip for the whole argument block.  The asm writes 0 (callers
+// add it to an index) and has no memory effects, so later loads keep the scalar path.
+__device__ __forceinline__ int fetch_args(const AttnArgs& a) {
+  int zero;
+  asm("s_mov_b32 %0, 0"
+      : "=s"(zero)
+      : "s"(a.q), "s"(a.k_cache), "s"(a.v_cache), "s"(a.block_table), "s"(a.prefix_len),
+        "s"(a.k_tree), "s"(a.v_tree), "s"(a.cu_nodes), "s"(a.anc), "s"(a.err), "s"(a.pair_order),
+        "s"(a.words), "s"(a.batch), "s"(a.max_nodes), "s"(a.max_prefix), "s"(a.num_blocks),
+        "s"(a.max_blocks), "s"(a.hq), "s"(a.hkv), "s"(a.group), "s"(a.splits),
+        "s"(a.blocks_per_split), "s"(a.row_tiles), "s"(a.total_work), "s"(a.scale));
+  return zero;
+}
+
+// Six 32-bit words through the scalar path, all six requests in flight at once
+// (one memory round trip); the addresses must be uniform across the wavefront.
+__device__ __forceinline__ void load_words6(const int32_t* p0, const int32_t* p1, const int32_t* p2,
+                                            const int32_t* p3, const int32_t* p4, const int32_t* p5,
+                                            int& v0, int& v1, int& v2, int& v3, int& v4, int& v5) {
+  asm volatile(
+      "s_load_dword %0, %6, 0x0\n\t"
+      "s_load_dword %1, %7, 0x0\n\t"
+      "s_load_dword %2, %8, 0x0\n\t"
+      "s_load_dword %3, %9, 0x0\n\t"
+      "s_load_dword %4, %10, 0x0\n\t"
+      "s_load_dword %5, %11, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3), "=&s"(v4), "=&s"(v5)
+      : "s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(p5)
+      : "memory");
+}
+
 // How one launch is laid out; the same function sizes the workspace.
 struct AttnPlan {
   bool mfma;          // bf16, head_dim 128: matrix-core kernel; else the vector kernel

@@ -486,30 +486,38 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
 
 // Merge of the prefix splits, one thread per (row, 4 consecutive d):
 //   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * out_s
-// All splits' values are loaded before any is used (one memory round trip).
+// All splits' values are loaded before any is used (one memory round trip); kS is
+// the split count rounded up to a power of two, the loads past the last split
+// re-read it and get weight zero.
+template <int kS>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
-  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  int zero;
+  asm("s_mov_b32 %0, 0"
+      : "=s"(zero)
+      : "s"(a.part_o), "s"(a.part_lse), "s"(a.out), "s"(a.lse), "s"(a.total_rows), "s"(a.splits));
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x + zero;
   if (idx >= static_cast<long>(a.total_rows) * (kD / 4)) return;
   const long gr = idx / (kD / 4);
   const int d4 = static_cast<int>(idx % (kD / 4));
-  float ls[kMaxSplits];
-  float4 ps[kMaxSplits];
+  float ls[kS];
+  float4 ps[kS];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) {
-    const bool on = sp < a.splits;
-    const long at = static_cast<long>(on ? sp : 0) * a.total_rows + gr;
+  for (int sp = 0; sp < kS; ++sp) {
+    const long at = static_cast<long>(min(sp, a.splits - 1)) * a.total_rows + gr;
     ls[sp] = a.part_lse[at];
     ps[sp] = *reinterpret_cast<const float4*>(a.part_o + at * kD + 4 * d4);
-    if (!on) ls[sp] = -INFINITY;
   }
+#pragma unroll
+  for (int sp = 0; sp < kS; ++sp)
+    if (sp >= a.splits) ls[sp] = -INFINITY;
   float mx = -INFINITY;
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) mx = fmaxf(mx, ls[sp]);
+  for (int sp = 0; sp < kS; ++sp) mx = fmaxf(mx, ls[sp]);
   const float mref = mx == -INFINITY ? 0.0f : mx;
   float w_sum = 0.0f;
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) {
+  for (int sp = 0; sp < kS; ++sp) {
     const float w = __builtin_amdgcn_exp2f((ls[sp] - mref) * kLog2e);
     w_sum += w;
     o.x = fmaf(w, ps[sp].x, o.x);
@@ -539,7 +547,16 @@ int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
 
 int launch_attn_combine(const AttnArgs& a, hipStream_t s) {
   const long items = static_cast<long>(a.total_rows) * (kD / 4);
-  hipLaunchKernelGGL(k_attn_combine, dim3(static_cast<int>((items + 255) / 256)), dim3(256), 0, s, a);
+  const dim3 grid(static_cast<int>((items + 255) / 256)), block(256);
+  static_assert(kMaxSplits == 16, "combine instances cover up to 16 splits");
+  if (a.splits <= 2)
+    hipLaunchKernelGGL(k_attn_combine<2>, grid, block, 0, s, a);
+  else if (a.splits <= 4)
+    hipLaunchKernelGGL(k_attn_combine<4>, grid, block, 0, s, a);
+  else if (a.splits <= 8)
+    hipLaunchKernelGGL(k_attn_combine<8>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_combine<16>, grid, block, 0, s, a);
   return check_launch("tree_verify_attention/combine");
 }
 

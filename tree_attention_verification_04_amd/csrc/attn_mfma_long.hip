@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   // ---- work item.  Pair rank r (in pair_order, longest first, when given) goes to
   // XCD r % 8; the m = row_tiles * splits work items of a pair get consecutive
   // dispatch slots of that XCD, so they run together and share its L2.
-  const int m_items = a.row_tiles * a.splits;
+  const int m_items = fetch_args(a) + a.row_tiles * a.splits;
   const int xcd = blockIdx.x % 8, k_slot = blockIdx.x / 8;
   const int rank = 8 * (k_slot / m_items) + xcd;
   if (rank >= a.batch * a.hkv) return;
@@ -134,9 +134,18 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   const int g = pair % a.hkv;
   const int b = pair / a.hkv;
 
-  const int n0 = a.cu_nodes[b];
-  int count = a.cu_nodes[b + 1] - n0;
-  int plen = a.prefix_len[b];
+  // the sequence's scalars and the block ids of the split's first tiles, requested
+  // together (the pipeline re-reads the ids; this brings their line in)
+  const int kb0 = split * a.blocks_per_split;
+  const int32_t* bt_first = a.max_blocks > 0 ? a.block_table + static_cast<long>(b) * a.max_blocks
+                                             : a.cu_nodes;  // any readable word
+  const int bt_last = max(a.max_blocks - 1, 0);
+  int n0, n1, plen, blk0, blk1, blk2;
+  load_words6(a.cu_nodes + b, a.cu_nodes + b + 1, a.prefix_len + b, bt_first + min(kb0, bt_last),
+              bt_first + min(kb0 + 1, bt_last), bt_first + min(kb0 + 2, bt_last), n0, n1, plen,
+              blk0, blk1, blk2);
+  (void)blk0, (void)blk1, (void)blk2;
+  int count = n1 - n0;
   const int tid = threadIdx.x;
   if (count > a.max_nodes) {
     if (tid == 0 && tile == 0 && split == 0) atomicOr(a.err, TV_ERR_TOO_MANY_NODES);
@@ -151,7 +160,6 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   if (r0 >= rows) return;
 
   const int nblk = (plen + kKT - 1) / kKT;
-  const int kb0 = split * a.blocks_per_split;
   const int kb1 = min(nblk, kb0 + a.blocks_per_split);
   const int n_prefix_tiles = max(0, kb1 - kb0);
   const bool do_tree = split == a.splits - 1;
