@@ -541,35 +541,42 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
 // the same clamped lengths the attention kernel uses.  One workgroup; rank of pair i
 // = number of pairs with a larger cost, or an equal cost and a smaller index.
 __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
-  __shared__ unsigned long long s_key[kMaxOrderedPairs];
+  __shared__ __attribute__((aligned(16))) uint32_t s_cost[kMaxOrderedPairs];
   const int pairs = a.batch * a.hkv;
-  for (int p = threadIdx.x; p < pairs; p += 1024) {
-    const int b = p / a.hkv;
-    const int n0 = a.cu_nodes[b];
-    const int count = max(0, min(a.cu_nodes[b + 1] - n0, a.max_nodes));
-    const int plen = max(0, min(a.prefix_len[b], min(a.max_prefix, a.max_blocks * 64)));
-    const int tiles = (plen + kKT - 1) / kKT + (count + 63) / 64;
-    const int rows = a.group * count;
-    int units = 0;
-    for (int t = 0; t < a.row_tiles; ++t) {
-      const int live = rows - t * kMfmaRowsPerWG;
-      if (live > 0) units += (min(live, kMfmaRowsPerWG) + 63) / 64;
+  const int padded = (pairs + 3) & ~3;
+  for (int p = threadIdx.x; p < padded; p += 1024) {
+    uint32_t cost = 0;  // padding entries: cost 0 and an index past every pair
+    if (p < pairs) {
+      const int b = p / a.hkv;
+      const int n0 = a.cu_nodes[b];
+      const int count = max(0, min(a.cu_nodes[b + 1] - n0, a.max_nodes));
+      const int plen = max(0, min(a.prefix_len[b], min(a.max_prefix, a.max_blocks * 64)));
+      const int tiles = (plen + kKT - 1) / kKT + (count + 63) / 64;
+      const int rows = a.group * count;
+      int units = 0;
+      for (int t = 0; t < a.row_tiles; ++t) {
+        const int live = rows - t * kMfmaRowsPerWG;
+        if (live > 0) units += (min(live, kMfmaRowsPerWG) + 63) / 64;
+      }
+      cost = static_cast<uint32_t>(tiles * units);
     }
-    s_key[p] = (static_cast<unsigned long long>(tiles) * units << 32) | static_cast<unsigned>(p);
+    s_cost[p] = cost;
   }
   __syncthreads();
-  // one wavefront per pair: its lanes count the larger keys, then sum the counts
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = wave; i < pairs; i += 1024 / 64) {
-    const unsigned ci = static_cast<unsigned>(s_key[i] >> 32);
+  // one thread per pair: its rank is the number of pairs that come first (larger
+  // cost, or equal cost and smaller index); every thread reads the same four
+  // costs at a time (an LDS broadcast)
+  for (int i = threadIdx.x; i < pairs; i += 1024) {
+    const uint32_t ci = s_cost[i];
     int rank = 0;
-    for (int j = lane; j < pairs; j += 64) {
-      const unsigned cj = static_cast<unsigned>(s_key[j] >> 32);
-      rank += (cj > ci) || (cj == ci && j < i);
+    for (int j = 0; j < padded; j += 4) {
+      const uint4 c = *reinterpret_cast<const uint4*>(&s_cost[j]);
+      rank += (c.x > ci) || (c.x == ci && j < i);
+      rank += (c.y > ci) || (c.y == ci && j + 1 < i);
+      rank += (c.z > ci) || (c.z == ci && j + 2 < i);
+      rank += (c.w > ci) || (c.w == ci && j + 3 < i);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) rank += __shfl_xor(rank, off, 64);
-    if (lane == 0) order[rank] = i;
+    order[rank] = i;
   }
 }
 
