@@ -366,6 +366,27 @@ def make_case(name: str, parents: list[np.ndarray], prefix_lens: list[int], hq: 
     return case
 
 
+def fp8_cache(cache: np.ndarray, dtype: int):
+    """An E4M3 copy of a K/V cache [num_blocks, hkv, 64, d] with one fp32 scale per
+    (block, head, position) row: scale = max|row| / 448 (1 for an all-zero row);
+    the bytes are torch's float8_e4m3fn cast of the row / scale, clamped to +-448.
+    Returns (codes uint8, scale float32 [num_blocks, hkv, 64])."""
+    import torch
+    x = to_f64(cache, dtype).astype(np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = np.clip(x / scale[..., None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, scale
+
+
+def fp8_random_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform E4M3 bytes over every finite code (0x7F and 0xFF, the NaNs, excluded)."""
+    c = rng.integers(0, 254, size=shape, dtype=np.int32)
+    c = c + (c >= 0x7F)  # skip 0x7F; 253 -> 254 stays below 0xFF
+    return c.astype(np.uint8)
+
+
 def add_probs(case: Case, seed: int, sigma2: float = 2.0) -> None:
     total, vocab = case.total_nodes, case.vocab
     case.p_target = prob_rows(seed, 1, total, vocab, sigma2)
