@@ -240,6 +240,59 @@ def measure_softmax(tv, case, reps: int) -> dict:
                 frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm")
 
 
+def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict | None:
+    """tree_verify_attention_fp8kv on this workload with its K/V cache quantized to E4M3
+    per (block, head, position) row, timed alone like the bf16 attention.  Algorithmic
+    bytes = the bf16 launch's with the prefix at 1 byte per element plus its 4-byte
+    scales.  None for a non-bf16 workload."""
+    import torch
+    import workloads as W
+    if case.dtype != W.DT_BF16 or case.d != 128:
+        return None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k8, ks = W.fp8_cache(case.k_cache, case.dtype)
+    v8, vs = W.fp8_cache(case.v_cache, case.dtype)
+    k8, v8, ks, vs = t(k8), t(v8), t(ks), t(vs)
+    out = torch.empty_like(dev["q"])
+    need = tv.tree_verify_attention_fp8kv_workspace_size(case.batch, case.total_nodes, mn,
+                                                         case.max_prefix, case.hq, case.hkv)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    run = lambda: tv.tree_verify_attention_fp8kv(
+        dev["q"], k8, v8, ks, vs, dev["block_table"], dev["prefix_len"], dev["k_tree"],
+        dev["v_tree"], dev["cu_nodes"], anc, mn, case.max_prefix, out=out, want_lse=False,
+        workspace=ws if need else None, err=err)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        times.append(s_ev.elapsed_time(e_ev) / reps)
+    if int(err.item()) != 0:
+        raise SystemExit(f"fp8 attention: device error word {int(err.item())}")
+    us = float(np.median(times)) * 1e3
+    bf16_bytes, _ = attention_cost(case)
+    prefix_tokens = int(case.prefix_len.sum())
+    if case.batch > 1 and np.all(case.block_table == case.block_table[:1]):
+        prefix_tokens = int(case.prefix_len.max())
+    bytes_ = bf16_bytes - prefix_tokens * case.hkv * (2 * case.d * 2 - 2 * (case.d + 4))
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return dict(us_per_launch=round(us, 3), bf16_us_per_launch=round(bf16_us, 3),
+                alg_bytes=int(bytes_), achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm",
+                kernel="register-staged matrix-core kernel (dequantizes into LDS)")
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -420,6 +473,7 @@ def main():
 
     commit = measure_commit(tv, case, dev, acc_out, max_path, reps)
     softmax = measure_softmax(tv, case, reps)
+    fp8 = measure_fp8(tv, case, dev, anc, mn, attn_us, reps)
 
     res = {
         "metric": "verified tree tokens/s",
@@ -442,7 +496,7 @@ def main():
                    "timing": "HIP-graph replay, events on the launch stream",
                    "wall_s": round(wall, 3)},
         "roofline": roof,
-        "next_rows": {"kv_commit": commit, "softmax_rows": softmax},
+        "next_rows": {"kv_commit": commit, "softmax_rows": softmax, "fp8_kv_attention": fp8},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

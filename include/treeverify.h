@@ -15,7 +15,9 @@
  *   tree_verify_attention every tree node attends to the shared paged prefix
  *                         and to its own ancestors (mask M_tree)
  *   tree_accept           ratio test, longest accepted path, residual resample
- * and a fourth that follows it:
+ * a variant of the second for an FP8 prefix cache:
+ *   tree_verify_attention_fp8kv
+ * and a fourth that follows them:
  *   tree_commit_kv        the accepted path's K/V become prefix positions
  *
  * Conventions shared by every call
@@ -141,6 +143,38 @@ int tree_verify_attention(const void* q, const void* k_cache, const void* v_cach
                           int32_t max_prefix, int32_t hq, int32_t hkv, int32_t head_dim,
                           int32_t dtype, float softmax_scale, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * tree_verify_attention_fp8kv — tree_verify_attention over an FP8 prefix cache.
+ *
+ * The paged cache holds OCP E4M3 bytes (4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, 0x7F/0xFF NaN) with one fp32 scale per block of 128
+ * elements, i.e. per (cache block, KV head, position) row of head_dim 128; the
+ * value of element d of a row is e4m3(byte) * scale ([P537] §9.2: Q, K, V in FP8
+ * E4M3 with block scaling, one scale per 128 elements, fp32 accumulators;
+ * appendix B: block scales beside K and V, applied when a block is loaded).  Only
+ * the streamed prefix is FP8: q, the tree K/V and out are bf16, head_dim is 128,
+ * and the result is tree_verify_attention's on the dequantized cache.  Each
+ * dequantized element is rounded once to bf16 before the matrix cores use it.
+ *
+ *   k_cache/v_cache [num_blocks, hkv, 64, 128] uint8 (E4M3)
+ *   k_scale/v_scale [num_blocks, hkv, 64] float (may be NULL when max_prefix == 0)
+ *   everything else as for tree_verify_attention with head_dim 128 and dtype
+ *   TV_DTYPE_BF16; workspace >= tree_verify_attention_fp8kv_workspace_size(...)
+ */
+size_t tree_verify_attention_fp8kv_workspace_size(int32_t batch, int32_t total_nodes,
+                                                  int32_t max_nodes, int32_t max_prefix,
+                                                  int32_t hq, int32_t hkv);
+
+int tree_verify_attention_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                const float* k_scale, const float* v_scale, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* prefix_len, const void* k_tree, const void* v_tree,
+                                const int32_t* cu_nodes, const uint64_t* anc_bits, int32_t words,
+                                int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                int32_t max_prefix, int32_t hq, int32_t hkv, float softmax_scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                int32_t* err, void* stream);
 
 /*
  * tree_accept — fused acceptance for every sequence, no host round-trip

@@ -90,6 +90,33 @@ def test_attention_host_checks(lib):
     assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128, tv.TV_DTYPE_BF16) == 8 * 8 * 4
 
 
+def fp8_call(lib, **kw):
+    one = ctypes.c_void_p(16)
+    args = dict(q=one, kc=one, vc=one, ks=one, vs=one, nblocks=4, bt=one, max_blocks=2, plen=one,
+                kt=one, vt=one, cu=one, anc=one, words=1, batch=1, total=3, max_nodes=3,
+                max_prefix=100, hq=4, hkv=2, scale=0.088, out=one, lse=None, ws=None, ws_bytes=0,
+                err=one, stream=None)
+    args.update(kw)
+    return lib.tree_verify_attention_fp8kv(*args.values())
+
+
+def test_fp8_attention_host_checks(lib):
+    assert fp8_call(lib, ks=None) == tv.TV_EINVAL               # a prefix needs its scales
+    assert fp8_call(lib, vs=None) == tv.TV_EINVAL
+    assert b"scales" in lib.tree_last_error()
+    assert fp8_call(lib, hq=3) == tv.TV_EINVAL
+    assert fp8_call(lib, max_prefix=200) == tv.TV_EINVAL
+    assert b"tree_verify_attention_fp8kv" in lib.tree_last_error()
+    assert fp8_call(lib, batch=0) == tv.TV_OK                  # nothing to do
+    # the FP8 cache runs the register-staged kernel: split partials, never a pair order
+    rows = 64 * 32
+    need = lib.tree_verify_attention_fp8kv_workspace_size(1, 64, 64, 1088, 32, 32)
+    assert need == ((5 * rows * 128 * 4 + 255) & ~255) + 5 * rows * 4   # 5 splits of 4 blocks
+    assert lib.tree_verify_attention_fp8kv_workspace_size(8, 4672, 584, 4096, 32, 8) == 0
+    assert fp8_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
+                    ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
+
+
 def test_accept_host_checks(lib):
     one = ctypes.c_void_p(16)
     need = lib.tree_accept_workspace_size(2, 1000)

@@ -38,6 +38,8 @@ EXPORTS = (
     "tree_build_index",
     "tree_verify_attention_workspace_size",
     "tree_verify_attention",
+    "tree_verify_attention_fp8kv_workspace_size",
+    "tree_verify_attention_fp8kv",
     "tree_accept_workspace_size",
     "tree_accept",
     "tree_commit_kv",
@@ -64,6 +66,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_attention.argtypes = [P, P, P, I, P, I, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                           I, F, P, P, P, Z, P, P]
     lib.tree_verify_attention.restype = ctypes.c_int
+    lib.tree_verify_attention_fp8kv_workspace_size.argtypes = [I] * 6
+    lib.tree_verify_attention_fp8kv_workspace_size.restype = Z
+    lib.tree_verify_attention_fp8kv.argtypes = [P, P, P, P, P, I, P, I, P, P, P, P, P, I, I, I, I,
+                                                I, I, I, F, P, P, P, Z, P, P]
+    lib.tree_verify_attention_fp8kv.restype = ctypes.c_int
     lib.tree_accept_workspace_size.argtypes = [I, I]
     lib.tree_accept_workspace_size.restype = Z
     lib.tree_accept.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P, P]
@@ -225,6 +232,68 @@ def tree_verify_attention(q, k_cache, v_cache, block_table, prefix_len, k_tree, 
                                      anc.shape[1], batch, total, max_nodes, max_prefix, hq, hkv,
                                      d, dt, scale, _ptr(out), _ptr(lse), _ptr(workspace),
                                      ws_bytes, _ptr(err), _stream(stream)))
+    return out, lse, err
+
+
+def tree_verify_attention_fp8kv_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
+                                               hkv) -> int:
+    return int(load().tree_verify_attention_fp8kv_workspace_size(batch, total_nodes, max_nodes,
+                                                                 max_prefix, hq, hkv))
+
+
+def tree_verify_attention_fp8kv(q, k_cache, v_cache, k_scale, v_scale, block_table, prefix_len,
+                                k_tree, v_tree, cu_nodes, anc, max_nodes: int, max_prefix: int,
+                                scale: float | None = None, *, out=None, lse=None,
+                                want_lse: bool = True, workspace=None, err=None, stream=None):
+    """Tree attention over an FP8 (E4M3) paged prefix cache with per-row scales.
+
+    q [total, hq, 128] bf16; k_cache/v_cache [num_blocks, hkv, 64, 128] uint8;
+    k_scale/v_scale [num_blocks, hkv, 64] float32; the rest as for
+    tree_verify_attention.  Returns (out, lse, err).
+    """
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, torch.uint8, 4)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, torch.float32, 3)
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        _need(t, name, torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_len, "prefix_len", torch.int32, 1)
+    _need(cu_nodes, "cu_nodes", torch.int32, 1)
+    _need(anc, "anc", torch.int64, 2)
+    total, hq, d = q.shape
+    num_blocks, hkv, blk, d2 = k_cache.shape
+    if d != 128 or blk != TV_BLOCK or d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks, hkv, 64, 128] and head_dim 128")
+    if tuple(k_scale.shape) != (num_blocks, hkv, blk) or tuple(v_scale.shape) != tuple(k_scale.shape):
+        raise ValueError("k_scale/v_scale must be [num_blocks, hkv, 64]")
+    if tuple(k_tree.shape) != (total, hkv, d) or tuple(v_tree.shape) != (total, hkv, d):
+        raise ValueError("k_tree/v_tree must be [total_nodes, hkv, head_dim]")
+    if anc.shape[0] != total:
+        raise ValueError("anc must have one row per node")
+    batch = cu_nodes.numel() - 1
+    if block_table.shape[0] != batch or prefix_len.numel() != batch:
+        raise ValueError("block_table / prefix_len must have one row per sequence")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((total, hq), dtype=torch.float32, device=q.device)
+    need = tree_verify_attention_fp8kv_workspace_size(batch, total, max_nodes, max_prefix, hq, hkv)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, q.device)
+    _check("tree_verify_attention_fp8kv",
+           lib.tree_verify_attention_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                           _ptr(v_scale), num_blocks, _ptr(block_table),
+                                           block_table.shape[1], _ptr(prefix_len), _ptr(k_tree),
+                                           _ptr(v_tree), _ptr(cu_nodes), _ptr(anc), anc.shape[1],
+                                           batch, total, max_nodes, max_prefix, hq, hkv, scale,
+                                           _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                           _ptr(err), _stream(stream)))
     return out, lse, err
 
 

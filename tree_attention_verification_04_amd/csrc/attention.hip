@@ -9,13 +9,14 @@
 // "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
 // (ufo.work/2026/537), appendix B).
 #include <algorithm>
+#include <cstdio>
 
 #include "attn.h"
 
 namespace tv {
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
-                        int head_dim, int dtype) {
+                        int head_dim, int dtype, bool fp8_kv) {
   AttnPlan p{};
   p.mfma = dtype == TV_DTYPE_BF16 && head_dim == 128;
   p.splits = 1;
@@ -40,7 +41,8 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
     p.splits = 1;
   }
   p.total_work = base * p.splits;
-  p.long_items = p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
+  // an FP8 prefix cache is dequantized by the register-staged kernel, whatever the length
+  p.long_items = !fp8_kv && p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
   // more long work items than compute units, from sequences of different lengths:
   // rank the (sequence, KV head) pairs by cost and start the longest first
   const long pairs = static_cast<long>(batch) * hkv;
@@ -67,54 +69,70 @@ extern "C" size_t tree_verify_attention_workspace_size(int32_t batch, int32_t to
                                                        int32_t hq, int32_t hkv, int32_t head_dim,
                                                        int32_t dtype) {
   if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return 0;
-  return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype)
+  return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype,
+                            false)
       .workspace;
 }
 
-extern "C" int tree_verify_attention(const void* q, const void* k_cache, const void* v_cache,
-                                     int32_t num_blocks, const int32_t* block_table,
-                                     int32_t max_blocks, const int32_t* prefix_len,
-                                     const void* k_tree, const void* v_tree,
-                                     const int32_t* cu_nodes, const uint64_t* anc_bits,
-                                     int32_t words, int32_t batch, int32_t total_nodes,
-                                     int32_t max_nodes, int32_t max_prefix, int32_t hq,
-                                     int32_t hkv, int32_t head_dim, int32_t dtype,
-                                     float softmax_scale, void* out, float* lse, void* workspace,
-                                     size_t workspace_bytes, int32_t* err, void* stream) {
-  tv::clear_error();
+extern "C" size_t tree_verify_attention_fp8kv_workspace_size(int32_t batch, int32_t total_nodes,
+                                                             int32_t max_nodes, int32_t max_prefix,
+                                                             int32_t hq, int32_t hkv) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return 0;
+  return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, 128,
+                            TV_DTYPE_BF16, true)
+      .workspace;
+}
+
+namespace {
+
+// Shared body of the bf16/fp32 and the FP8-cache entry points (fp8 false: the
+// cache has the dtype of q and no scales).
+int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cache,
+                     const void* v_cache, const float* k_scale, const float* v_scale,
+                     int32_t num_blocks,
+                     const int32_t* block_table, int32_t max_blocks, const int32_t* prefix_len,
+                     const void* k_tree, const void* v_tree, const int32_t* cu_nodes,
+                     const uint64_t* anc_bits, int32_t words, int32_t batch, int32_t total_nodes,
+                     int32_t max_nodes, int32_t max_prefix, int32_t hq, int32_t hkv,
+                     int32_t head_dim, int32_t dtype, float softmax_scale, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, int32_t* err, void* stream) {
+  char msg[160];
+  auto bad = [&](int status, const char* what) {
+    snprintf(msg, sizeof(msg), "%s: %s", fn, what);
+    return tv::fail(status, msg);
+  };
   if (batch < 0 || total_nodes < 0 || max_prefix < 0 || num_blocks < 0 || max_blocks < 0)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: negative size");
+    return bad(TV_EINVAL, "negative size");
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: hq must be a positive multiple of hkv");
-  if (head_dim != 64 && head_dim != 128)
-    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: head_dim must be 64 or 128");
+    return bad(TV_EINVAL, "hq must be a positive multiple of hkv");
+  if (head_dim != 64 && head_dim != 128) return bad(TV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (dtype != TV_DTYPE_F32 && dtype != TV_DTYPE_BF16)
-    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: dtype must be F32 or BF16");
+    return bad(TV_EUNSUPPORTED, "dtype must be F32 or BF16");
   if (max_nodes < 1 || max_nodes > TV_MAX_NODES)
-    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: max_nodes must be in [1, 2048]");
-  if (words < tv::ceil_div(max_nodes, 64))
-    return tv::fail(TV_EINVAL, "tree_verify_attention: words < ceil(max_nodes / 64)");
+    return bad(TV_EUNSUPPORTED, "max_nodes must be in [1, 2048]");
+  if (words < tv::ceil_div(max_nodes, 64)) return bad(TV_EINVAL, "words < ceil(max_nodes / 64)");
   if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: softmax_scale must be positive and finite");
-  if (err == nullptr || cu_nodes == nullptr)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: null err or cu_nodes");
+    return bad(TV_EINVAL, "softmax_scale must be positive and finite");
+  if (err == nullptr || cu_nodes == nullptr) return bad(TV_EINVAL, "null err or cu_nodes");
   if (batch == 0 || total_nodes == 0) return TV_OK;
   if (q == nullptr || k_tree == nullptr || v_tree == nullptr || anc_bits == nullptr ||
       out == nullptr || prefix_len == nullptr)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: null q, tree K/V, anc_bits, out or prefix_len");
+    return bad(TV_EINVAL, "null q, tree K/V, anc_bits, out or prefix_len");
   if (max_prefix > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
-    return tv::fail(TV_EINVAL, "tree_verify_attention: null paged cache or block table");
+    return bad(TV_EINVAL, "null paged cache or block table");
+  if (max_prefix > 0 && fp8 && (k_scale == nullptr || v_scale == nullptr))
+    return bad(TV_EINVAL, "null cache scales");
   if (max_prefix > 0 && num_blocks < 1)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: max_prefix > 0 needs num_blocks >= 1");
+    return bad(TV_EINVAL, "max_prefix > 0 needs num_blocks >= 1");
   if (static_cast<long>(max_blocks) * 64 < max_prefix)
-    return tv::fail(TV_EINVAL, "tree_verify_attention: max_prefix exceeds max_blocks * 64");
+    return bad(TV_EINVAL, "max_prefix exceeds max_blocks * 64");
   if (static_cast<long>(total_nodes) * hq > INT32_MAX)
-    return tv::fail(TV_EUNSUPPORTED, "tree_verify_attention: too many (node, head) rows");
+    return bad(TV_EUNSUPPORTED, "too many (node, head) rows");
 
   const tv::AttnPlan plan =
-      tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype);
+      tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, fp8);
   if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
-    return tv::fail(TV_EWORKSPACE, "tree_verify_attention: workspace missing or too small");
+    return bad(TV_EWORKSPACE, "workspace missing or too small");
 
   tv::AttnArgs a{};
   a.q = q;
@@ -126,6 +144,10 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
   a.v_tree = v_tree;
   a.cu_nodes = cu_nodes;
   a.anc = anc_bits;
+  if (fp8) {  // the kernel choice keys on a non-null scale pointer
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+  }
   a.out = out;
   a.lse = lse;
   a.err = err;
@@ -161,4 +183,39 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
     a.pair_order = order;
   }
   return plan.long_items ? tv::launch_attn_long(a, s) : tv::launch_attn_mfma(a, s);
+}
+
+}  // namespace
+
+extern "C" int tree_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                                     int32_t num_blocks, const int32_t* block_table,
+                                     int32_t max_blocks, const int32_t* prefix_len,
+                                     const void* k_tree, const void* v_tree,
+                                     const int32_t* cu_nodes, const uint64_t* anc_bits,
+                                     int32_t words, int32_t batch, int32_t total_nodes,
+                                     int32_t max_nodes, int32_t max_prefix, int32_t hq,
+                                     int32_t hkv, int32_t head_dim, int32_t dtype,
+                                     float softmax_scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, int32_t* err, void* stream) {
+  tv::clear_error();
+  return verify_attention("tree_verify_attention", false, q, k_cache, v_cache, nullptr, nullptr,
+                          num_blocks, block_table, max_blocks, prefix_len, k_tree, v_tree,
+                          cu_nodes, anc_bits, words, batch, total_nodes, max_nodes, max_prefix, hq,
+                          hkv, head_dim, dtype, softmax_scale, out, lse, workspace,
+                          workspace_bytes, err, stream);
+}
+
+extern "C" int tree_verify_attention_fp8kv(
+    const void* q, const uint8_t* k_cache, const uint8_t* v_cache, const float* k_scale,
+    const float* v_scale, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+    const int32_t* prefix_len, const void* k_tree, const void* v_tree, const int32_t* cu_nodes,
+    const uint64_t* anc_bits, int32_t words, int32_t batch, int32_t total_nodes,
+    int32_t max_nodes, int32_t max_prefix, int32_t hq, int32_t hkv, float softmax_scale,
+    void* out, float* lse, void* workspace, size_t workspace_bytes, int32_t* err, void* stream) {
+  tv::clear_error();
+  return verify_attention("tree_verify_attention_fp8kv", true, q, k_cache, v_cache, k_scale,
+                          v_scale, num_blocks, block_table,
+                          max_blocks, prefix_len, k_tree, v_tree, cu_nodes, anc_bits, words, batch,
+                          total_nodes, max_nodes, max_prefix, hq, hkv, 128, TV_DTYPE_BF16,
+                          softmax_scale, out, lse, workspace, workspace_bytes, err, stream);
 }

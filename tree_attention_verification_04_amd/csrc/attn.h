@@ -22,6 +22,8 @@ struct AttnArgs {
   float* part_lse;          // [splits, total_rows]
   int32_t* err;
   const int* pair_order;    // [batch * hkv] (sequence, KV head) pairs, longest first; or null
+  const float* k_scale;     // FP8 prefix cache: [num_blocks, hkv, 64] scales; null for bf16
+  const float* v_scale;
   int words, batch, total_nodes, total_rows, max_nodes, max_prefix;
   int num_blocks, max_blocks, hq, hkv, group;
   int splits, blocks_per_split, row_tiles, total_work;
@@ -76,7 +78,7 @@ struct AttnPlan {
 };
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
-                        int head_dim, int dtype);
+                        int head_dim, int dtype, bool fp8_kv);
 
 int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);

@@ -42,15 +42,17 @@ constexpr int kThreads = kWaves * 64;
 static_assert(kMfmaRowsPerWG == kWaves * 32, "row tile is 32 rows per wavefront");
 
 using TileRegs = TileRegsT<kThreads>;
-__device__ __forceinline__ void load_tile(const TileSrc& src, int tid, TileRegs& r) {
-  load_tile_t<kThreads>(src, tid, r);
-}
-__device__ __forceinline__ void store_tile(char* stage, uint64_t* anc_slot, int tid, TileRegs& r,
-                                           int nvalid) {
-  store_tile_t<kThreads>(stage, anc_slot, tid, r, nvalid);
-}
 
+// kFp8: the paged prefix cache holds E4M3 bytes with one scale per (block, KV
+// head, position); its tiles are dequantized to bf16 on their way into LDS and
+// everything after that is the bf16 kernel.
+template <bool kFp8>
 __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
+  auto load_tile = [](const TileSrc& src, int tid, TileRegs& r) __attribute__((always_inline)) {
+    load_tile_t<kThreads, kFp8>(src, tid, r);
+  };
+  auto store_tile = [](char* stage, uint64_t* anc_slot, int tid, TileRegs& r, int nvalid)
+      __attribute__((always_inline)) { store_tile_t<kThreads, kFp8>(stage, anc_slot, tid, r, nvalid); };
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kAncOff + 3 * kAncBytes);
   int* s_simd_slots = reinterpret_cast<int*>(smem + kAncOff + 3 * kAncBytes + 16);  // [4]
@@ -158,20 +160,32 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
     tile_kind(it, kind, base);
     TileSrc s;
     s.anc = stage_anc + (kind == 1 ? base : 0);
+    s.ks = nullptr;
+    s.vs = nullptr;
     if (kind == 0) {
+      // an FP8 row is 128 bytes: 64 16-bit units
+      constexpr int kRowUnits = kFp8 ? kD / 2 : kD;
       const int blk = bt_row[base / kKT];
+      if (kFp8) {
+        s.ks = a.k_scale;
+        s.vs = a.v_scale;
+      }
       if (blk < 0 || blk >= a.num_blocks) {
         if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
         s.k = kc;
         s.v = vc;
-        s.row_stride = kD;
+        s.row_stride = kRowUnits;
         s.nvalid = 0;
         return s;
       }
-      const long off = (static_cast<long>(blk) * a.hkv + g) * kKT * kD;
-      s.k = kc + off;
-      s.v = vc + off;
-      s.row_stride = kD;
+      const long row0 = (static_cast<long>(blk) * a.hkv + g) * kKT;  // first (block, head) row
+      s.k = kc + row0 * kRowUnits;
+      s.v = vc + row0 * kRowUnits;
+      if (kFp8) {
+        s.ks = a.k_scale + row0;
+        s.vs = a.v_scale + row0;
+      }
+      s.row_stride = kRowUnits;
       s.nvalid = min(kKT, plen - base);
     } else {
       const long off = (static_cast<long>(n0 + base * 64) * a.hkv + g) * kD;
@@ -534,12 +548,17 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
     attr_set = true;
   }
   const int grid = 8 * ceil_div(a.total_work, 8);
-  hipLaunchKernelGGL(k_attn_mfma, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
+  if (a.k_scale != nullptr)
+    hipLaunchKernelGGL(k_attn_mfma<true>, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_mfma<false>, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
   const int st = check_launch("tree_verify_attention/mfma");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);
