@@ -251,6 +251,21 @@ def sample_tokens(seed: int, p: np.ndarray, chunk: int = 64) -> np.ndarray:
     return tok
 
 
+def draft_rows(rng: np.random.Generator, batch: int, rows: int, k: int, vocab: int = 32000,
+               sigma2: float = 2.0) -> np.ndarray:
+    """Synthetic draft-model top-K rows: the K largest probabilities, in descending
+    order, of softmax(N(0, sigma2) logits over `vocab`) (softmax in fp64, then fp32).
+    Returns [batch, rows, k] float32."""
+    out = np.empty((batch, rows, k), np.float32)
+    sd = math.sqrt(sigma2)
+    for b in range(batch):
+        for r in range(rows):
+            x = rng.standard_normal(vocab) * sd
+            e = np.exp(x - x.max())
+            out[b, r] = (np.sort(e)[::-1][:k] / e.sum()).astype(np.float32)
+    return out
+
+
 def grid_uniforms(rng: np.random.Generator, n: int) -> np.ndarray:
     """Uniforms on the 2^-24 grid: exactly representable, in [0, 1)."""
     m = rng.integers(0, 1 << 24, size=n, dtype=np.int64)
