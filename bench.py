@@ -293,6 +293,48 @@ def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict 
                 kernel="register-staged matrix-core kernel (dequantizes into LDS)")
 
 
+def measure_draft_tree(tv, case, reps: int) -> dict:
+    """tree_draft_build for this workload's batch and tree size (at most 256 nodes),
+    top-K 8, beta 0.7, depth <= 6, prune ratio 0.1, on synthetic top-K rows; timed
+    alone.  The draws are serial within a sequence: a latency-bound row."""
+    import torch
+    import workloads as W
+    n_max = max(1, min(256, case.max_nodes))
+    rng = np.random.default_rng(11)
+    probs = torch.from_numpy(W.draft_rows(rng, case.batch, n_max + 1, 8, vocab=4096)).cuda()
+    u = torch.from_numpy(np.stack([W.grid_uniforms(rng, n_max) for _ in range(case.batch)])
+                         .astype(np.float32)).cuda()
+    out = [torch.empty((case.batch, n_max), dtype=torch.int32, device="cuda") for _ in range(2)]
+    qd = torch.empty((case.batch, n_max), dtype=torch.float32, device="cuda")
+    cnt = torch.empty(case.batch, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    run = lambda: tv.tree_draft_build(probs, u, 6, 0.7, 0.1, parent=out[0], slot=out[1],
+                                      q_draft=qd, count=cnt, err=err)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        times.append(s_ev.elapsed_time(e_ev) / reps)
+    if int(err.item()) != 0:
+        raise SystemExit(f"draft tree: device error word {int(err.item())}")
+    us = float(np.median(times)) * 1e3
+    nodes = int(cnt.sum().item())
+    return dict(us_per_call=round(us, 3), batch=case.batch, n_max=n_max, nodes_built=nodes,
+                nodes_per_s=round(nodes / (us * 1e-6), 1), bound="latency",
+                note="one wavefront per sequence; draws are serial within a sequence")
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -474,6 +516,7 @@ def main():
     commit = measure_commit(tv, case, dev, acc_out, max_path, reps)
     softmax = measure_softmax(tv, case, reps)
     fp8 = measure_fp8(tv, case, dev, anc, mn, attn_us, reps)
+    draft = measure_draft_tree(tv, case, reps)
 
     res = {
         "metric": "verified tree tokens/s",
@@ -496,7 +539,8 @@ def main():
                    "timing": "HIP-graph replay, events on the launch stream",
                    "wall_s": round(wall, 3)},
         "roofline": roof,
-        "next_rows": {"kv_commit": commit, "softmax_rows": softmax, "fp8_kv_attention": fp8},
+        "next_rows": {"kv_commit": commit, "softmax_rows": softmax, "fp8_kv_attention": fp8,
+                      "draft_tree": draft},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

@@ -17,6 +17,8 @@
  *   tree_accept           ratio test, longest accepted path, residual resample
  * a variant of the second for an FP8 prefix cache:
  *   tree_verify_attention_fp8kv
+ * one that builds the tree before them:
+ *   tree_draft_build      draft top-K rows -> parent array of the candidate tree
  * and a fourth that follows them:
  *   tree_commit_kv        the accepted path's K/V become prefix positions
  *
@@ -69,6 +71,7 @@ extern "C" {
 #define TV_ERR_PATH 32           /* accepted path longer than max_path */
 #define TV_ERR_UNIFORM 64        /* a uniform outside [0, 1) or NaN */
 #define TV_ERR_ROW 128           /* a context-row index outside [0, ctx_rows) */
+#define TV_ERR_DRAFT 256         /* a draft probability outside [0, 1] or NaN */
 
 /* element types */
 #define TV_DTYPE_F32 0
@@ -175,6 +178,43 @@ int tree_verify_attention_fp8kv(const void* q, const uint8_t* k_cache, const uin
                                 int32_t max_prefix, int32_t hq, int32_t hkv, float softmax_scale,
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 int32_t* err, void* stream);
+
+/*
+ * tree_draft_build — the candidate tree of each sequence from the draft model's
+ * top-K rows, before the step: importance-sampled expansion ([P500] §3.1: weights
+ * w = p^beta / sum p^beta over a context's top-K, branches kept and deepened by
+ * sampling on w) after a cumulative-mass soft truncation ([P525] §2.1.2: in
+ * descending order, keep candidates until their mass reaches 1 - prune_ratio,
+ * renormalise the kept ones by that mass).
+ *
+ * Per sequence: row 0 of probs is the context at the end of the prefix, row i+1
+ * the context after node i.  A context's kept candidates (the shortest leading
+ * run of slots whose fp64 mass reaches 1 - prune_ratio) get path weight = parent's
+ * path weight * p^beta / (sum over the kept slots of p^beta).  Node i is drawn
+ * from all candidates not yet taken with probability proportional to path weight:
+ * the first candidate, in creation order, whose running sum exceeds
+ * u[i] * (sum of all); if its depth < max_depth and row i+1 exists, its kept
+ * children become candidates.  Building stops at n_max nodes or when no
+ * candidate has weight.  The decision arithmetic is fp64; a draw whose
+ * threshold falls within rounding of a running-sum boundary may resolve either
+ * way (the sums are chunked across a wavefront).
+ *
+ *   probs     [batch, rows, k] float, each row non-increasing, values in [0, 1]
+ *   u         [batch, n_max] float in [0, 1)
+ *   k <= 16, n_max <= 256, max_depth in [1, 256], beta >= 0, prune_ratio in [0, 1]
+ *   parent    out [batch, n_max] int32: local parent (-1 = the prefix), -2 past count
+ *   slot      out [batch, n_max] int32: the top-K slot of the node's token, -2 past count
+ *   q_draft   out [batch, n_max] float: p / kept mass of its context (the draft
+ *             probability the acceptance test must use for the node), 0 past count
+ *   count     out [batch] int32: nodes built (parents precede children, so
+ *             parent[b][0 .. count-1] is a valid tree_build_index input)
+ *   err       TV_ERR_DRAFT (a probability outside [0, 1]), TV_ERR_UNIFORM; such a
+ *             sequence builds nothing
+ */
+int tree_draft_build(const float* probs, const float* u, int32_t batch, int32_t rows, int32_t k,
+                     int32_t n_max, int32_t max_depth, float beta, float prune_ratio,
+                     int32_t* parent, int32_t* slot, float* q_draft, int32_t* count, int32_t* err,
+                     void* stream);
 
 /*
  * tree_accept — fused acceptance for every sequence, no host round-trip

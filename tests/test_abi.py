@@ -117,6 +117,28 @@ def test_fp8_attention_host_checks(lib):
                     ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
 
 
+def test_draft_build_host_checks(lib):
+    one = ctypes.c_void_p(16)
+
+    def call(**kw):
+        args = dict(probs=one, u=one, batch=2, rows=65, k=8, n_max=64, depth=6, beta=0.7,
+                    ratio=0.1, parent=one, slot=one, q=one, count=one, err=one, stream=None)
+        args.update(kw)
+        return lib.tree_draft_build(*args.values())
+
+    assert call(k=17) == tv.TV_EUNSUPPORTED
+    assert call(n_max=257) == tv.TV_EUNSUPPORTED
+    assert call(k=0) == tv.TV_EINVAL
+    assert call(depth=0) == tv.TV_EINVAL
+    assert call(beta=-0.5) == tv.TV_EINVAL
+    assert call(beta=float("inf")) == tv.TV_EINVAL
+    assert call(ratio=1.5) == tv.TV_EINVAL
+    assert call(err=None) == tv.TV_EINVAL
+    assert call(probs=None) == tv.TV_EINVAL
+    assert b"tree_draft_build" in lib.tree_last_error()
+    assert call(batch=0) == tv.TV_OK
+
+
 def test_accept_host_checks(lib):
     one = ctypes.c_void_p(16)
     need = lib.tree_accept_workspace_size(2, 1000)

@@ -30,6 +30,7 @@ TV_ERR_ZERO_MASS = 16
 TV_ERR_PATH = 32
 TV_ERR_UNIFORM = 64
 TV_ERR_ROW = 128
+TV_ERR_DRAFT = 256
 TV_DTYPE_F32, TV_DTYPE_BF16 = 0, 1
 TV_MAX_NODES = 2048
 TV_BLOCK = 64
@@ -40,6 +41,7 @@ EXPORTS = (
     "tree_verify_attention",
     "tree_verify_attention_fp8kv_workspace_size",
     "tree_verify_attention_fp8kv",
+    "tree_draft_build",
     "tree_accept_workspace_size",
     "tree_accept",
     "tree_commit_kv",
@@ -71,6 +73,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_attention_fp8kv.argtypes = [P, P, P, P, P, I, P, I, P, P, P, P, P, I, I, I, I,
                                                 I, I, I, F, P, P, P, Z, P, P]
     lib.tree_verify_attention_fp8kv.restype = ctypes.c_int
+    lib.tree_draft_build.argtypes = [P, P, I, I, I, I, I, F, F, P, P, P, P, P, P]
+    lib.tree_draft_build.restype = ctypes.c_int
     lib.tree_accept_workspace_size.argtypes = [I, I]
     lib.tree_accept_workspace_size.restype = Z
     lib.tree_accept.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P, P]
@@ -295,6 +299,35 @@ def tree_verify_attention_fp8kv(q, k_cache, v_cache, k_scale, v_scale, block_tab
                                            _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                            _ptr(err), _stream(stream)))
     return out, lse, err
+
+
+def tree_draft_build(probs, u, max_depth: int, beta: float, prune_ratio: float, *, parent=None,
+                     slot=None, q_draft=None, count=None, err=None, stream=None):
+    """Candidate trees from draft top-K rows.  probs [batch, rows, k] float32
+    (rows non-increasing), u [batch, n_max] float32 in [0, 1).  Returns
+    (parent, slot, q_draft, count, err); see tree_draft_build in treeverify.h."""
+    lib = load()
+    _need(probs, "probs", torch.float32, 3)
+    _need(u, "u", torch.float32, 2)
+    batch, rows, k = probs.shape
+    if u.shape[0] != batch:
+        raise ValueError("u must have one row per sequence")
+    n_max = u.shape[1]
+    dev = probs.device
+    if parent is None:
+        parent = torch.empty((batch, n_max), dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty((batch, n_max), dtype=torch.int32, device=dev)
+    if q_draft is None:
+        q_draft = torch.empty((batch, n_max), dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(batch, dtype=torch.int32, device=dev)
+    err = _err_word(err, dev)
+    _check("tree_draft_build",
+           lib.tree_draft_build(_ptr(probs), _ptr(u), batch, rows, k, n_max, max_depth,
+                                float(beta), float(prune_ratio), _ptr(parent), _ptr(slot),
+                                _ptr(q_draft), _ptr(count), _ptr(err), _stream(stream)))
+    return parent, slot, q_draft, count, err
 
 
 def tree_accept_workspace_size(batch: int, vocab: int) -> int:
