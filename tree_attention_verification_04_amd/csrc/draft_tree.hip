@@ -18,7 +18,7 @@
 // the candidates (in creation order) live in LDS, so a draw waits on no global
 // memory.  A draw
 // sums the weights in 64 contiguous chunks (one per lane), scans the chunk sums
-// across the wavefront, and the lane whose chunk holds u * total walks it.  The
+// across the wavefront (DPP), and the lane whose chunk holds u * total walks it.  The
 // truncation and the normaliser of the weights are summed by one lane in slot
 // order; powers are one per lane.  Everything that decides a draw is fp64 with
 // no contraction.
@@ -45,6 +45,44 @@ struct DraftArgs {
   int rows, k, n_max, max_depth;
   float beta, prune;
 };
+
+// x of lane (lane - shift) combined by DPP (ctrl / row mask), 0 where there is no
+// source lane or the row is masked off; fp64 moves as two 32-bit halves
+__device__ __forceinline__ double dpp_shift(double x, int ctrl, int row_mask) {
+  const int lo = __double2loint(x), hi = __double2hiint(x);
+  int lo2, hi2;
+  switch (ctrl) {  // the DPP control must be a constant
+#define TV_DPP(c)                                                          \
+  case c:                                                                  \
+    lo2 = __builtin_amdgcn_update_dpp(0, lo, c, 0xf, 0xf, true);           \
+    hi2 = __builtin_amdgcn_update_dpp(0, hi, c, 0xf, 0xf, true);           \
+    break;
+    TV_DPP(0x111) TV_DPP(0x112) TV_DPP(0x114) TV_DPP(0x118) TV_DPP(0x138)
+#undef TV_DPP
+    case 0x142:  // row_bcast:15 into rows 1 and 3
+      lo2 = __builtin_amdgcn_update_dpp(0, lo, 0x142, 0xa, 0xf, false);
+      hi2 = __builtin_amdgcn_update_dpp(0, hi, 0x142, 0xa, 0xf, false);
+      break;
+    default:  // 0x143, row_bcast:31 into rows 2 and 3
+      lo2 = __builtin_amdgcn_update_dpp(0, lo, 0x143, 0xc, 0xf, false);
+      hi2 = __builtin_amdgcn_update_dpp(0, hi, 0x143, 0xc, 0xf, false);
+      break;
+  }
+  (void)row_mask;
+  return __hiloint2double(hi2, lo2);
+}
+
+// inclusive prefix sum over the 64 lanes: shifts 1, 2, 4, 8 inside each 16-lane
+// row, then the row totals broadcast into the rows after them
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x += dpp_shift(x, 0x111, 0xf);
+  x += dpp_shift(x, 0x112, 0xf);
+  x += dpp_shift(x, 0x114, 0xf);
+  x += dpp_shift(x, 0x118, 0xf);
+  x += dpp_shift(x, 0x142, 0xa);
+  x += dpp_shift(x, 0x143, 0xc);
+  return x;
+}
 
 // candidate info: context node + 1 (9 bits), slot (4 bits); depth comes from the node
 __device__ __forceinline__ uint16_t pack_info(int ctx, int slot) {
@@ -161,15 +199,10 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
     const int c0 = min(n_cand, lane * chunk), c1 = min(n_cand, c0 + chunk);
     double ls = 0.0;
     for (int j = c0; j < c1; ++j) ls += s_w[j];
-    double incl = ls;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
-    const double total = __shfl(incl, 63, 64);
+    const double incl = wave_incl_scan(ls);
+    const double excl = dpp_shift(incl, 0x138, 0xf);  // wave_shr:1; lane 0 gets 0
+    const double total = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(incl), 63),
+                                          __builtin_amdgcn_readlane(__double2loint(incl), 63));
     if (!(total > 0.0)) break;
     const double t = static_cast<double>(s_u[n]) * total;
     const unsigned long long over = __ballot(incl > t);
