@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The native library bound through ctypes, on a GPU machine only."""
+    """The native library bound through ctypes, on a machine with a GPU only."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")

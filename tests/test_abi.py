@@ -22,7 +22,7 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(tv.LIB_PATH):
-        pytest.fail("libtreeverify.so is not built (run __graft_entry__.build())")
+        pytest.fail("libtreeverify.so is not built (run python -m tree_attention_verification_04_amd.build)")
     return tv.load()
 
 
