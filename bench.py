@@ -108,13 +108,14 @@ def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> 
     copy_w = max((sum(v) / len(v) for k, v in w.items() if "add" in k.lower() and "elementwise" in k), default=None)
     sf = COPY_BYTES / (copy_f * 1024.0)
     sw = COPY_BYTES / (copy_w * 1024.0)
-    # one tree_verify_attention launch: its main kernel plus the split merge and the
-    # pair-order kernel when the plan uses them
+    # one tree_verify_attention launch: its main kernel plus the split merge, the
+    # pair-order kernel and the ticket clear when the plan uses them
     main_keys = ("k_attn_long", "k_attn_mfma", "k_attn_vec")
     attn_f = next((v for v in (pick(f, k) for k in main_keys) if v is not None), 0.0)
     attn_w = next((v for v in (pick(w, k) for k in main_keys) if v is not None), 0.0)
-    comb_f = (pick(f, "k_attn_combine") or 0.0) + (pick(f, "k_attn_order") or 0.0)
-    comb_w = (pick(w, "k_attn_combine") or 0.0) + (pick(w, "k_attn_order") or 0.0)
+    aux = ("k_attn_combine", "k_attn_order", "k_clear_words")
+    comb_f = sum(pick(f, k) or 0.0 for k in aux)
+    comb_w = sum(pick(w, k) or 0.0 for k in aux)
     fetch = (attn_f + comb_f) * 1024.0 * sf
     write = (attn_w + comb_w) * 1024.0 * sw
     with open(traffic_path(config), "w") as fh:

@@ -124,6 +124,39 @@ def test_attention_small(gpu_lib, name):
     check_attention(gpu_lib, case, TOL_F32 if dt == W.DT_F32 else TOL_BF16)
 
 
+TAIL_CASES = {
+    # 64 (sequence, KV head) pairs x 10 row tiles: 16 items per die are cut in 2
+    # prefix pieces; sequences with no prefix, a single node, no nodes
+    "pieces2": ([W.tree_kary_levels(8, 3)] * 5 + [W.tree_random(np.random.default_rng(12), 300, 8),
+                 W.tree_chain(1), np.zeros(0, np.int32)], [300, 0, 4096, 64, 65, 1000, 130, 5],
+                32, 8),
+    # 8 pairs x 33 row tiles: one item per die, cut in 7 pieces, most of them with no
+    # prefix tile (2 blocks); the last piece holds only tree tiles
+    "pieces7_short": ([W.tree_random(np.random.default_rng(13), 1025, 12)], [100], 64, 8),
+    "pieces7_long": ([W.tree_random(np.random.default_rng(14), 1025, 12)], [2000], 64, 8),
+    # 2056 pairs (more than the ordering kernel ranks) x 1 row tile: the last item of
+    # each die (sequence 256) cut in 7 pieces, its tickets cleared by a kernel of their own
+    "pieces7_unordered": ([W.tree_heap(63)] * 257, [200 + 3 * (b % 50) for b in range(257)], 32,
+                          8),
+}
+TAIL_SEQS = {"pieces7_unordered": {0, 100, 255, 256}}
+
+
+@pytest.mark.parametrize("name", sorted(TAIL_CASES))
+def test_attention_tail_pieces(gpu_lib, name):
+    """Work items of the last round cut into prefix pieces and merged by the piece that
+    finishes last; a second call (tickets cleared again) gives the same bits."""
+    parents, plens, hq, hkv = TAIL_CASES[name]
+    case = W.make_case(name, parents, plens, hq, hkv, 128, W.DT_BF16, 10, 21, with_probs=False)
+    nodes = sample_nodes(case, 10, seed=5, seqs=TAIL_SEQS.get(name))
+    out = check_attention(gpu_lib, case, TOL_BF16, nodes=nodes)
+    dev = W.case_to_device(case, probs=False)
+    anc, _, _, _ = gpu_index(gpu_lib, case, dev)
+    again, _, _ = gpu_attention(gpu_lib, case, dev, anc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+
+
 def test_attention_aliased_block_tables(gpu_lib):
     parents = [W.tree_kary_levels(3, 3)] * 4
     case = W.make_case("alias", parents, [700] * 4, 8, 2, 128, W.DT_BF16, 10, 3, alias_prefix=True,

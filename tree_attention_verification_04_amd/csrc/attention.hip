@@ -23,6 +23,7 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   p.blocks_per_split = 0;
   p.row_tiles = 0;
   p.total_work = 0;
+  p.tail_pieces = 1;
   p.workspace = 0;
   if (!p.mfma || batch <= 0 || hkv <= 0) return p;
   const int group = hq / hkv;
@@ -47,6 +48,26 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   // rank the (sequence, KV head) pairs by cost and start the longest first
   const long pairs = static_cast<long>(batch) * hkv;
   p.ordered = p.long_items && batch > 1 && p.total_work > kCUs && pairs <= kMaxOrderedPairs;
+  // tail balancing: each die runs its pairs' work items in order on its compute
+  // units; when the items do not fill the last round evenly, the items of that
+  // round are cut into prefix pieces, so the last round ends sooner
+  p.tail_pieces = 1;
+  p.tail_whole = 0;
+  p.tail_items = 0;
+  if (p.long_items && p.splits == 1) {
+    const long per_die = ceil_div(static_cast<int>(pairs), kXCDs) * static_cast<long>(p.row_tiles);
+    if (per_die > kCUsPerXCD && per_die <= INT32_MAX / kMaxTailPieces) {
+      const int tail = static_cast<int>(per_die % kCUsPerXCD);
+      const int k = tail_pieces_for(tail, kCUsPerXCD);
+      if (k > 1) {
+        p.tail_pieces = k;
+        p.tail_items = tail;
+        p.tail_whole = static_cast<int>(per_die) - tail;
+        // the ordering kernel also clears the tail tickets (no launch of its own)
+        if (pairs <= kMaxOrderedPairs) p.ordered = true;
+      }
+    }
+  }
   size_t ws = 0;
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(total_nodes) * hq;
@@ -54,12 +75,36 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
     const size_t l_bytes = static_cast<size_t>(p.splits) * rows * sizeof(float);
     ws = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
   }
+  if (p.tail_pieces > 1) {  // partials [8 * tail_items * pieces * 256 rows] (out, lse), tickets
+    const size_t prow = static_cast<size_t>(kXCDs) * p.tail_items * p.tail_pieces * kMfmaRowsPerWG;
+    ws = ((prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)) +
+         prow * sizeof(float);
+    p.tail_off = (ws + 255) & ~static_cast<size_t>(255);
+    ws = p.tail_off + static_cast<size_t>(kXCDs) * p.tail_items * sizeof(int);
+  }
   if (p.ordered) {
     p.order_off = (ws + 255) & ~static_cast<size_t>(255);
     ws = p.order_off + static_cast<size_t>(pairs) * sizeof(int);
   }
   p.workspace = ws;
   return p;
+}
+
+// The last round holds `tail` items on `cus` units.  Cut into k pieces each, it
+// takes ceil(tail * k / cus) rounds of 1/k of an item; every cut piece also
+// writes and re-reads a partial result, charged as 2% of an item.
+int tail_pieces_for(int tail, int cus) {
+  if (tail <= 0 || cus <= 0) return 1;
+  int best_k = 1;
+  float best = 1.0f;
+  for (int k = 2; k <= kMaxTailPieces; ++k) {
+    const float t = static_cast<float>(ceil_div(tail * k, cus)) / k + 0.02f * (k - 1);
+    if (t < best - 1e-6f) {
+      best = t;
+      best_k = k;
+    }
+  }
+  return best_k;
 }
 
 }  // namespace tv
@@ -173,6 +218,17 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
     a.part_o = static_cast<float*>(workspace);
     const size_t o_pad = (o_bytes + 255) & ~static_cast<size_t>(255);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_pad);
+  }
+  a.tail_pieces = plan.tail_pieces;
+  a.tail_whole = plan.tail_whole;
+  a.tail_items = plan.tail_items;
+  if (plan.tail_pieces > 1) {
+    const size_t prow =
+        static_cast<size_t>(tv::kXCDs) * plan.tail_items * plan.tail_pieces * tv::kMfmaRowsPerWG;
+    a.part_o = static_cast<float*>(workspace);
+    const size_t o_pad = (prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_pad);
+    a.tail_cnt = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.tail_off);
   }
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);

@@ -24,9 +24,14 @@ struct AttnArgs {
   const int* pair_order;    // [batch * hkv] (sequence, KV head) pairs, longest first; or null
   const float* k_scale;     // FP8 prefix cache: [num_blocks, hkv, 64] scales; null for bf16
   const float* v_scale;
+  int* tail_cnt;            // [8 * tail_items] finish tickets of the split tail items
   int words, batch, total_nodes, total_rows, max_nodes, max_prefix;
   int num_blocks, max_blocks, hq, hkv, group;
   int splits, blocks_per_split, row_tiles, total_work;
+  // tail balancing (pipelined kernel, splits == 1): per XCD, work items
+  // [0, tail_whole) run whole and the next tail_items are cut into tail_pieces
+  // prefix ranges each, merged by the piece that finishes last (1 = off)
+  int tail_pieces, tail_whole, tail_items;
   float scale;              // softmax scale (natural-exp units)
 };
 
@@ -42,7 +47,8 @@ __device__ __forceinline__ int fetch_args(const AttnArgs& a) {
         "s"(a.k_tree), "s"(a.v_tree), "s"(a.cu_nodes), "s"(a.anc), "s"(a.err), "s"(a.pair_order),
         "s"(a.words), "s"(a.batch), "s"(a.max_nodes), "s"(a.max_prefix), "s"(a.num_blocks),
         "s"(a.max_blocks), "s"(a.hq), "s"(a.hkv), "s"(a.group), "s"(a.splits),
-        "s"(a.blocks_per_split), "s"(a.row_tiles), "s"(a.total_work), "s"(a.scale));
+        "s"(a.blocks_per_split), "s"(a.row_tiles), "s"(a.total_work), "s"(a.scale),
+        "s"(a.tail_pieces), "s"(a.tail_whole), "s"(a.tail_items));
   return zero;
 }
 
@@ -73,8 +79,12 @@ struct AttnPlan {
   int blocks_per_split;
   int row_tiles;      // row tiles per (sequence, kv head)
   long total_work;    // workgroups with work
+  int tail_pieces;    // tail balancing: pieces per tail item (1 = off)
+  int tail_whole;     // per XCD: work items that run whole
+  int tail_items;     // per XCD: work items cut into tail_pieces pieces
   size_t workspace;   // bytes of split partials and of the pair order
   size_t order_off;   // workspace offset of the pair order
+  size_t tail_off;    // workspace offset of the tail tickets (partials start at 0)
 };
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
@@ -86,8 +96,15 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s);
 int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s);
 int launch_attn_combine(const AttnArgs& a, hipStream_t s);
 
+// Tail balancing: how many pieces to cut each of `tail` leftover work items into
+// so that the last round on `cus` compute units ends soonest (1 = leave whole).
+int tail_pieces_for(int tail, int cus);
+
 constexpr int kMfmaRowsPerWG = 256;  // 8 waves x 32 rows
 constexpr int kCUs = 256;
+constexpr int kXCDs = 8;             // compute dies; workgroup i runs on die i % 8
+constexpr int kCUsPerXCD = kCUs / kXCDs;
+constexpr int kMaxTailPieces = 8;
 constexpr int kMaxSplits = 16;       // prefix splits per (sequence, KV head, row tile)
 // work items of at least this many 64-key tiles run the pipelined kernel
 #ifndef TV_LONG_MIN_TILES

@@ -122,37 +122,51 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
 
   // ---- work item.  Pair rank r (in pair_order, longest first, when given) goes to
   // XCD r % 8; the m = row_tiles * splits work items of a pair get consecutive
-  // dispatch slots of that XCD, so they run together and share its L2.
+  // dispatch slots of that XCD, so they run together and share its L2.  With tail
+  // balancing (splits == 1), the XCD's items past tail_whole are each cut into
+  // tail_pieces consecutive slots, one prefix range per piece.
   const int m_items = fetch_args(a) + a.row_tiles * a.splits;
-  const int xcd = blockIdx.x % 8, k_slot = blockIdx.x / 8;
-  const int rank = 8 * (k_slot / m_items) + xcd;
+  const int xcd = blockIdx.x % kXCDs, k_slot = blockIdx.x / kXCDs;
+  int item = k_slot / m_items, member = k_slot % m_items, piece = 0, pieces = 1, tail_slot = -1;
+  if (a.tail_pieces > 1 && k_slot >= a.tail_whole) {
+    const int t = k_slot - a.tail_whole;
+    const int idx = a.tail_whole + t / a.tail_pieces;
+    item = idx / a.row_tiles;
+    member = idx % a.row_tiles;
+    piece = t % a.tail_pieces;
+    pieces = a.tail_pieces;
+    tail_slot = xcd * a.tail_items + t / a.tail_pieces;
+  }
+  const int rank = kXCDs * item + xcd;
   if (rank >= a.batch * a.hkv) return;
   const int pair = a.pair_order != nullptr ? a.pair_order[rank] : rank;
-  const int member = k_slot % m_items;
   const int tile = member % a.row_tiles;
   const int split = member / a.row_tiles;
   const int g = pair % a.hkv;
   const int b = pair / a.hkv;
+  const bool first_piece = split == 0 && piece == 0;
 
   // the sequence's scalars and the block ids of the split's first tiles, requested
-  // together (the pipeline re-reads the ids; this brings their line in)
-  const int kb0 = split * a.blocks_per_split;
+  // together (the pipeline re-reads the ids; this brings their line in); a tail
+  // piece's range depends on the prefix length, so its guess uses max_prefix
+  const int kb0_guess = pieces > 1 ? piece * ceil_div(ceil_div(a.max_prefix, kKT), pieces)
+                                   : split * a.blocks_per_split;
   const int32_t* bt_first = a.max_blocks > 0 ? a.block_table + static_cast<long>(b) * a.max_blocks
                                              : a.cu_nodes;  // any readable word
   const int bt_last = max(a.max_blocks - 1, 0);
   int n0, n1, plen, blk0, blk1, blk2;
-  load_words6(a.cu_nodes + b, a.cu_nodes + b + 1, a.prefix_len + b, bt_first + min(kb0, bt_last),
-              bt_first + min(kb0 + 1, bt_last), bt_first + min(kb0 + 2, bt_last), n0, n1, plen,
-              blk0, blk1, blk2);
+  load_words6(a.cu_nodes + b, a.cu_nodes + b + 1, a.prefix_len + b,
+              bt_first + min(kb0_guess, bt_last), bt_first + min(kb0_guess + 1, bt_last),
+              bt_first + min(kb0_guess + 2, bt_last), n0, n1, plen, blk0, blk1, blk2);
   (void)blk0, (void)blk1, (void)blk2;
   int count = n1 - n0;
   const int tid = threadIdx.x;
   if (count > a.max_nodes) {
-    if (tid == 0 && tile == 0 && split == 0) atomicOr(a.err, TV_ERR_TOO_MANY_NODES);
+    if (tid == 0 && tile == 0 && first_piece) atomicOr(a.err, TV_ERR_TOO_MANY_NODES);
     count = a.max_nodes;
   }
   if (plen < 0 || plen > a.max_prefix || plen > a.max_blocks * 64) {
-    if (tid == 0 && tile == 0 && split == 0) atomicOr(a.err, TV_ERR_BLOCK);
+    if (tid == 0 && tile == 0 && first_piece) atomicOr(a.err, TV_ERR_BLOCK);
     plen = max(0, min(plen, min(a.max_prefix, a.max_blocks * 64)));
   }
   const int rows = a.group * count;
@@ -160,9 +174,11 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   if (r0 >= rows) return;
 
   const int nblk = (plen + kKT - 1) / kKT;
-  const int kb1 = min(nblk, kb0 + a.blocks_per_split);
+  const int span = pieces > 1 ? ceil_div(nblk, pieces) : a.blocks_per_split;
+  const int kb0 = pieces > 1 ? piece * span : split * a.blocks_per_split;
+  const int kb1 = min(nblk, kb0 + span);
   const int n_prefix_tiles = max(0, kb1 - kb0);
-  const bool do_tree = split == a.splits - 1;
+  const bool do_tree = split == a.splits - 1 && piece == pieces - 1;
 
   // ---- rows: wavefront w owns rows 32 w .. 32 w + 31 of the tile
   const int wave = tid >> 6, lane = tid & 63;
@@ -488,11 +504,76 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
     wait_loads_and_barrier<0>();
   }
 
-  // ---- epilogue (each lane holds half of its row's sum)
+  // ---- epilogue (each lane holds half of its row's sum and d = 32 dt + 8 qd + 4 half
+  // + 0..3 of its row's output)
   const float l_tot = l + __shfl_xor(l, 32, 64);
+  float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  float lse = l_tot > 0.0f ? m_out * a.scale + logf(l_tot) : -INFINITY;
+  if (pieces > 1) {
+    // a piece of a tail item: store the piece's normalised output and log-sum-exp,
+    // then take a ticket; the piece that takes the last one merges all pieces.  The
+    // others' stores are visible to it: every lane's stores complete before the
+    // barrier, one thread then releases them at device scope (the die's L2 is written
+    // back) and takes the ticket; the merging piece's ticket thread acquires (caches
+    // invalidated) before the barrier that starts the merge.  One fence per workgroup
+    // rather than per lane: each fence writes back or invalidates the whole L2 of the
+    // die, which the other work items of the pair are reading their K/V tiles from.
+    const long p_base = static_cast<long>(tail_slot) * pieces * kMfmaRowsPerWG + rl;
+    if (row_ok) {
+      float* po = a.part_o + (p_base + static_cast<long>(piece) * kMfmaRowsPerWG) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<float4*>(po + 32 * dt + 8 * qd + 4 * half) =
+              make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv,
+                          acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv);
+      if (half == 0) a.part_lse[p_base + static_cast<long>(piece) * kMfmaRowsPerWG] = lse;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int* s_last = reinterpret_cast<int*>(smem + kMaskOff + 4);
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      *s_last = atomicAdd(a.tail_cnt + tail_slot, 1) == pieces - 1;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (*s_last == 0) return;
+    if (!row_ok) return;
+    // lse = log sum_p exp(lse_p), out = sum_p exp(lse_p - lse) out_p
+    float lp[kMaxTailPieces];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pc = 0; pc < kMaxTailPieces; ++pc) {
+      lp[pc] = pc < pieces ? a.part_lse[p_base + static_cast<long>(pc) * kMfmaRowsPerWG] : -INFINITY;
+      mx = fmaxf(mx, lp[pc]);
+    }
+    const float mref = mx == -INFINITY ? 0.0f : mx;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16_t{};
+    float w_sum = 0.0f;
+#pragma unroll
+    for (int pc = 0; pc < kMaxTailPieces; ++pc) {
+      if (pc >= pieces) break;
+      const float w = __builtin_amdgcn_exp2f((lp[pc] - mref) * kLog2e);
+      w_sum += w;
+      const float* po = a.part_o + (p_base + static_cast<long>(pc) * kMfmaRowsPerWG) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const float4 x = *reinterpret_cast<const float4*>(po + 32 * dt + 8 * qd + 4 * half);
+          acc[dt][4 * qd] = fmaf(w, x.x, acc[dt][4 * qd]);
+          acc[dt][4 * qd + 1] = fmaf(w, x.y, acc[dt][4 * qd + 1]);
+          acc[dt][4 * qd + 2] = fmaf(w, x.z, acc[dt][4 * qd + 2]);
+          acc[dt][4 * qd + 3] = fmaf(w, x.w, acc[dt][4 * qd + 3]);
+        }
+    }
+    inv = w_sum > 0.0f ? 1.0f / w_sum : 0.0f;
+    lse = w_sum > 0.0f ? mx + logf(w_sum) : -INFINITY;
+  }
   if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse = l_tot > 0.0f ? m_out * a.scale + logf(l_tot) : -INFINITY;
   if (a.splits == 1) {
     uint16_t* out = static_cast<uint16_t*>(a.out) + grow * kD;
 #pragma unroll
@@ -520,6 +601,13 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   }
 }
 
+// zero n words (the finish tickets of the tail items; a kernel rather than a
+// memset, so that the launch can be captured in a graph)
+__global__ void __launch_bounds__(256) k_clear_words(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 int launch_attn_long(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
@@ -527,22 +615,35 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
     attr_set = true;
   }
-  const int grid = 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
+  int grid = 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
+  if (a.tail_pieces > 1) {
+    if (a.pair_order == nullptr) {  // else the ordering kernel has cleared the tickets
+      const int n_tickets = kXCDs * a.tail_items;
+      hipLaunchKernelGGL(k_clear_words, dim3(ceil_div(n_tickets, 256)), dim3(256), 0, s,
+                         a.tail_cnt, n_tickets);
+      const int st = check_launch("tree_verify_attention/tickets");
+      if (st != TV_OK) return st;
+    }
+    grid = kXCDs * (a.tail_whole + a.tail_items * a.tail_pieces);
+  }
   hipLaunchKernelGGL(k_attn_long, dim3(grid), dim3(kTL), kSmemL, s, a);
   const int st = check_launch("tree_verify_attention/long");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);
 }
 
-// ---- dispatch order of the long work items: the (sequence, KV head) pairs ranked
-// by estimated cost, largest first (longest-processing-time-first list scheduling;
-// the hardware hands each freed compute unit the next workgroup in dispatch order).
+// ---- dispatch order of the long work items (and, with tail balancing, the clear of
+// the finish tickets): the (sequence, KV head) pairs ranked by estimated cost,
+// largest first (longest-processing-time-first list scheduling; the hardware hands
+// each freed compute unit the next workgroup in dispatch order).
 // Cost of a pair = its tiles x its live 64-row units summed over its row tiles, from
 // the same clamped lengths the attention kernel uses.  One workgroup; rank of pair i
 // = number of pairs with a larger cost, or an equal cost and a smaller index.
 __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
   __shared__ __attribute__((aligned(16))) uint32_t s_cost[kMaxOrderedPairs];
   const int pairs = a.batch * a.hkv;
+  if (a.tail_pieces > 1)  // the finish tickets of the tail items start at zero
+    for (int i = threadIdx.x; i < kXCDs * a.tail_items; i += 1024) a.tail_cnt[i] = 0;
   const int padded = (pairs + 3) & ~3;
   for (int p = threadIdx.x; p < padded; p += 1024) {
     uint32_t cost = 0;  // padding entries: cost 0 and an index past every pair

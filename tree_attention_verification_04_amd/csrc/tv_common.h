@@ -26,7 +26,7 @@ inline int check_launch(const char* what) {
   return TV_OK;
 }
 
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- device side
 
