@@ -83,22 +83,26 @@ def test_attention_host_checks(lib):
     assert attn_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
                      ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
     assert b"workspace" in lib.tree_last_error()
-    # the fp32 path needs no workspace; one long work item per (sequence, KV head) needs
-    # none either; more long items than compute units that fill the last round evenly
-    # need the pair order only
+    # the fp32 path needs no workspace; one long work item per (sequence, KV head) and
+    # compute unit needs none either
     assert lib.tree_verify_attention_workspace_size(1, 15, 15, 128, 4, 4, 64, tv.TV_DTYPE_F32) == 0
     assert lib.tree_verify_attention_workspace_size(4, 1024, 256, 32768, 64, 8, 128, tv.TV_DTYPE_BF16) == 0
-    assert lib.tree_verify_attention_workspace_size(64, 5000, 96, 4096, 32, 8, 128, tv.TV_DTYPE_BF16) == 512 * 4
-    # 64 (sequence, KV head) pairs x 10 row tiles = 80 items per die of 32 compute units:
-    # the 16 items of the last round are cut in 2 pieces, each with a 256-row partial
-    # (128 fp32 outputs + 1 log-sum-exp per row) and one finish ticket per item, then
+    # more long items than compute units run persistently: 8 queue heads (one per die),
+    # then (256-byte aligned) the pair order; 512 pairs x 2 row tiles fill every die's
+    # last round, so nothing is cut
+    assert lib.tree_verify_attention_workspace_size(64, 5000, 96, 4096, 32, 8, 128,
+                                                    tv.TV_DTYPE_BF16) == 256 + 512 * 4
+    # 64 pairs x 10 row tiles = 80 items per die of 32 compute units: the 16 items of the
+    # last round are cut in 2 pieces, each with a 256-row partial (128 fp32 outputs + 1
+    # log-sum-exp per row); then 8 queue heads and one finish ticket per cut item, then
     # the pair order
     rows = 8 * 16 * 2 * 256
     tail = rows * 128 * 4 + rows * 4
-    tickets_end = tail + 8 * 16 * 4
-    assert tail % 256 == 0 and tickets_end % 256 == 0
+    counters_end = tail + (8 + 8 * 16) * 4
+    order_off = (counters_end + 255) // 256 * 256
+    assert tail % 256 == 0
     assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128,
-                                                    tv.TV_DTYPE_BF16) == tickets_end + 64 * 4
+                                                    tv.TV_DTYPE_BF16) == order_off + 64 * 4
 
 
 def fp8_call(lib, **kw):

@@ -24,6 +24,9 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   p.row_tiles = 0;
   p.total_work = 0;
   p.tail_pieces = 1;
+  p.persistent = false;
+  p.die_slots = 0;
+  p.n_counters = 0;
   p.workspace = 0;
   if (!p.mfma || batch <= 0 || hkv <= 0) return p;
   const int group = hq / hkv;
@@ -48,26 +51,32 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   // rank the (sequence, KV head) pairs by cost and start the longest first
   const long pairs = static_cast<long>(batch) * hkv;
   p.ordered = p.long_items && batch > 1 && p.total_work > kCUs && pairs <= kMaxOrderedPairs;
-  // tail balancing: each die runs its pairs' work items in order on its compute
-  // units; when the items do not fill the last round evenly, the items of that
-  // round are cut into prefix pieces, so the last round ends sooner
+  // Long items over more than one round run persistently: one workgroup per compute
+  // unit pulls its die's items from a queue head (then other dies' items), so that a
+  // die whose units are all busy does not hold up the dispatch of the others (the
+  // hardware hands workgroups to dies in launch order).  Each die's queue holds its
+  // pairs' items, pair-major; per die, die_slots queue slots.
   p.tail_pieces = 1;
   p.tail_whole = 0;
   p.tail_items = 0;
-  if (p.long_items && p.splits == 1) {
-    const long per_die = ceil_div(static_cast<int>(pairs), kXCDs) * static_cast<long>(p.row_tiles);
-    if (per_die > kCUsPerXCD && per_die <= INT32_MAX / kMaxTailPieces) {
-      const int tail = static_cast<int>(per_die % kCUsPerXCD);
-      const int k = tail_pieces_for(tail, kCUsPerXCD);
-      if (k > 1) {
-        p.tail_pieces = k;
-        p.tail_items = tail;
-        p.tail_whole = static_cast<int>(per_die) - tail;
-        // the ordering kernel also clears the tail tickets (no launch of its own)
-        if (pairs <= kMaxOrderedPairs) p.ordered = true;
-      }
+  const long per_die = ceil_div(static_cast<int>(pairs), kXCDs) * static_cast<long>(p.row_tiles) *
+                       p.splits;
+  p.die_slots = per_die <= INT32_MAX / kMaxTailPieces ? static_cast<int>(per_die) : 0;
+  p.persistent = p.long_items && p.die_slots > kCUsPerXCD;
+  // tail balancing: when a die's items do not fill its last round evenly, the items
+  // of that round are cut into prefix pieces, so the last round ends sooner
+  if (p.persistent && p.splits == 1) {
+    const int tail = p.die_slots % kCUsPerXCD;
+    const int k = tail_pieces_for(tail, kCUsPerXCD);
+    if (k > 1) {
+      p.tail_pieces = k;
+      p.tail_items = tail;
+      p.tail_whole = p.die_slots - tail;
+      p.die_slots = p.tail_whole + tail * k;
     }
   }
+  // the ordering kernel also clears the queue heads and tickets (no launch of its own)
+  if (p.persistent && pairs <= kMaxOrderedPairs) p.ordered = true;
   size_t ws = 0;
   if (p.splits > 1) {
     const size_t rows = static_cast<size_t>(total_nodes) * hq;
@@ -75,12 +84,16 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
     const size_t l_bytes = static_cast<size_t>(p.splits) * rows * sizeof(float);
     ws = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
   }
-  if (p.tail_pieces > 1) {  // partials [8 * tail_items * pieces * 256 rows] (out, lse), tickets
+  if (p.tail_pieces > 1) {  // partials [8 * tail_items * pieces * 256 rows] (out, lse)
     const size_t prow = static_cast<size_t>(kXCDs) * p.tail_items * p.tail_pieces * kMfmaRowsPerWG;
     ws = ((prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)) +
          prow * sizeof(float);
-    p.tail_off = (ws + 255) & ~static_cast<size_t>(255);
-    ws = p.tail_off + static_cast<size_t>(kXCDs) * p.tail_items * sizeof(int);
+  }
+  p.n_counters = 0;
+  if (p.persistent) {  // 8 queue heads, then one finish ticket per tail item
+    p.n_counters = kXCDs + kXCDs * p.tail_items;
+    p.counters_off = (ws + 255) & ~static_cast<size_t>(255);
+    ws = p.counters_off + static_cast<size_t>(p.n_counters) * sizeof(int);
   }
   if (p.ordered) {
     p.order_off = (ws + 255) & ~static_cast<size_t>(255);
@@ -222,13 +235,19 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
   a.tail_pieces = plan.tail_pieces;
   a.tail_whole = plan.tail_whole;
   a.tail_items = plan.tail_items;
+  a.die_slots = plan.die_slots;
   if (plan.tail_pieces > 1) {
     const size_t prow =
         static_cast<size_t>(tv::kXCDs) * plan.tail_items * plan.tail_pieces * tv::kMfmaRowsPerWG;
     a.part_o = static_cast<float*>(workspace);
     const size_t o_pad = (prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_pad);
-    a.tail_cnt = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.tail_off);
+  }
+  if (plan.persistent) {
+    a.counters = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.counters_off);
+    a.n_counters = plan.n_counters;
+    a.queue = a.counters;
+    a.tail_cnt = a.counters + tv::kXCDs;
   }
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);

@@ -24,14 +24,18 @@ struct AttnArgs {
   const int* pair_order;    // [batch * hkv] (sequence, KV head) pairs, longest first; or null
   const float* k_scale;     // FP8 prefix cache: [num_blocks, hkv, 64] scales; null for bf16
   const float* v_scale;
-  int* tail_cnt;            // [8 * tail_items] finish tickets of the split tail items
+  int* counters;            // persistent launch: [n_counters] words the launch zeroes first
+  int* queue;               // = counters: [8] queue heads, one per die
+  int* tail_cnt;            // = counters + 8: [8 * tail_items] finish tickets of the tail items
   int words, batch, total_nodes, total_rows, max_nodes, max_prefix;
   int num_blocks, max_blocks, hq, hkv, group;
   int splits, blocks_per_split, row_tiles, total_work;
-  // tail balancing (pipelined kernel, splits == 1): per XCD, work items
+  // tail balancing (pipelined kernel, splits == 1): per die, work items
   // [0, tail_whole) run whole and the next tail_items are cut into tail_pieces
   // prefix ranges each, merged by the piece that finishes last (1 = off)
   int tail_pieces, tail_whole, tail_items;
+  int die_slots;            // queue slots per die (persistent launch)
+  int n_counters;
   float scale;              // softmax scale (natural-exp units)
 };
 
@@ -48,7 +52,7 @@ __device__ __forceinline__ int fetch_args(const AttnArgs& a) {
         "s"(a.words), "s"(a.batch), "s"(a.max_nodes), "s"(a.max_prefix), "s"(a.num_blocks),
         "s"(a.max_blocks), "s"(a.hq), "s"(a.hkv), "s"(a.group), "s"(a.splits),
         "s"(a.blocks_per_split), "s"(a.row_tiles), "s"(a.total_work), "s"(a.scale),
-        "s"(a.tail_pieces), "s"(a.tail_whole), "s"(a.tail_items));
+        "s"(a.tail_pieces), "s"(a.tail_whole), "s"(a.tail_items), "s"(a.die_slots));
   return zero;
 }
 
@@ -79,12 +83,15 @@ struct AttnPlan {
   int blocks_per_split;
   int row_tiles;      // row tiles per (sequence, kv head)
   long total_work;    // workgroups with work
+  bool persistent;    // long items over several rounds: one workgroup per CU pulls items
+  int die_slots;      // queue slots per die
   int tail_pieces;    // tail balancing: pieces per tail item (1 = off)
-  int tail_whole;     // per XCD: work items that run whole
-  int tail_items;     // per XCD: work items cut into tail_pieces pieces
-  size_t workspace;   // bytes of split partials and of the pair order
+  int tail_whole;     // per die: work items that run whole
+  int tail_items;     // per die: work items cut into tail_pieces pieces
+  int n_counters;     // queue heads + tail tickets
+  size_t workspace;   // bytes of split or tail partials, counters and the pair order
   size_t order_off;   // workspace offset of the pair order
-  size_t tail_off;    // workspace offset of the tail tickets (partials start at 0)
+  size_t counters_off;  // workspace offset of the counters (partials start at 0)
 };
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,

@@ -116,17 +116,17 @@ struct Slot {
 
 }  // namespace
 
-__global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
+// One work item: slot k_slot of die xcd's list.
+__device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, const int k_slot) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kMaskOff);
 
   // ---- work item.  Pair rank r (in pair_order, longest first, when given) goes to
-  // XCD r % 8; the m = row_tiles * splits work items of a pair get consecutive
-  // dispatch slots of that XCD, so they run together and share its L2.  With tail
-  // balancing (splits == 1), the XCD's items past tail_whole are each cut into
+  // die r % 8; the m = row_tiles * splits work items of a pair get consecutive
+  // slots of that die's list, so they run together and share its L2.  With tail
+  // balancing (splits == 1), the die's items past tail_whole are each cut into
   // tail_pieces consecutive slots, one prefix range per piece.
   const int m_items = fetch_args(a) + a.row_tiles * a.splits;
-  const int xcd = blockIdx.x % kXCDs, k_slot = blockIdx.x / kXCDs;
   int item = k_slot / m_items, member = k_slot % m_items, piece = 0, pieces = 1, tail_slot = -1;
   if (a.tail_pieces > 1 && k_slot >= a.tail_whole) {
     const int t = k_slot - a.tail_whole;
@@ -601,8 +601,45 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   }
 }
 
-// zero n words (the finish tickets of the tail items; a kernel rather than a
-// memset, so that the launch can be captured in a graph)
+// Without a queue, workgroup i runs slot i / 8 of die i % 8's list (the hardware
+// hands workgroups to dies round-robin in launch order).  With one (items over
+// several rounds), one workgroup per compute unit takes slots from the queue of
+// the die it runs on (the hardware die id) until it is empty, then from the other
+// dies' queues: no unit idles while another die's dispatch waits, and no
+// workgroup ever waits for another.
+__global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int* s_pull = reinterpret_cast<int*>(smem + kMaskOff + 8);
+  const bool queued = a.queue != nullptr;
+  const int home = static_cast<int>(__builtin_amdgcn_s_getreg(20 | (3 << 11))) & (kXCDs - 1);
+  int die = queued ? home : static_cast<int>(blockIdx.x % kXCDs);
+  int k_slot = blockIdx.x / kXCDs, tried = 0;
+  for (;;) {  // one call site of the item body (register pressure)
+    if (queued) {
+      if (threadIdx.x == 0) *s_pull = atomicAdd(a.queue + die, 1);
+      __syncthreads();
+      k_slot = *s_pull;
+      __syncthreads();  // every lane has read the slot before lane 0 takes the next
+      if (k_slot >= a.die_slots) {
+        if (++tried == kXCDs) break;
+        die = (die + 1) & (kXCDs - 1);
+        continue;
+      }
+    }
+    // the item body reads its arguments afresh from the kernel-argument segment (the
+    // pointer is opaque to the compiler), so that no argument stays in a scalar
+    // register across items: the body alone needs nearly all of them
+    const __attribute__((address_space(4))) char* ap =
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    const AttnArgs item_args = *(const AttnArgs*)ap;
+    long_item(item_args, die, k_slot);
+    if (!queued) break;
+  }
+}
+
+// zero n words (the counters of a persistent launch; a kernel rather than a memset,
+// so that the launch can be captured in a graph)
 __global__ void __launch_bounds__(256) k_clear_words(int* p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -616,15 +653,14 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
     attr_set = true;
   }
   int grid = 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
-  if (a.tail_pieces > 1) {
-    if (a.pair_order == nullptr) {  // else the ordering kernel has cleared the tickets
-      const int n_tickets = kXCDs * a.tail_items;
-      hipLaunchKernelGGL(k_clear_words, dim3(ceil_div(n_tickets, 256)), dim3(256), 0, s,
-                         a.tail_cnt, n_tickets);
-      const int st = check_launch("tree_verify_attention/tickets");
+  if (a.queue != nullptr) {
+    if (a.pair_order == nullptr) {  // else the ordering kernel has cleared the counters
+      hipLaunchKernelGGL(k_clear_words, dim3(ceil_div(a.n_counters, 256)), dim3(256), 0, s,
+                         a.counters, a.n_counters);
+      const int st = check_launch("tree_verify_attention/counters");
       if (st != TV_OK) return st;
     }
-    grid = kXCDs * (a.tail_whole + a.tail_items * a.tail_pieces);
+    grid = kCUs;
   }
   hipLaunchKernelGGL(k_attn_long, dim3(grid), dim3(kTL), kSmemL, s, a);
   const int st = check_launch("tree_verify_attention/long");
@@ -632,18 +668,18 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
   return launch_attn_combine(a, s);
 }
 
-// ---- dispatch order of the long work items (and, with tail balancing, the clear of
-// the finish tickets): the (sequence, KV head) pairs ranked by estimated cost,
-// largest first (longest-processing-time-first list scheduling; the hardware hands
-// each freed compute unit the next workgroup in dispatch order).
+// ---- dispatch order of the long work items (and, for a persistent launch, the
+// clear of its queue heads and finish tickets): the (sequence, KV head) pairs
+// ranked by estimated cost, largest first (longest-processing-time-first list
+// scheduling: each free compute unit takes the next item of its die's list).
 // Cost of a pair = its tiles x its live 64-row units summed over its row tiles, from
 // the same clamped lengths the attention kernel uses.  One workgroup; rank of pair i
 // = number of pairs with a larger cost, or an equal cost and a smaller index.
 __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
   __shared__ __attribute__((aligned(16))) uint32_t s_cost[kMaxOrderedPairs];
   const int pairs = a.batch * a.hkv;
-  if (a.tail_pieces > 1)  // the finish tickets of the tail items start at zero
-    for (int i = threadIdx.x; i < kXCDs * a.tail_items; i += 1024) a.tail_cnt[i] = 0;
+  if (a.counters != nullptr)  // queue heads and tail tickets of a persistent launch start at zero
+    for (int i = threadIdx.x; i < a.n_counters; i += 1024) a.counters[i] = 0;
   const int padded = (pairs + 3) & ~3;
   for (int p = threadIdx.x; p < padded; p += 1024) {
     uint32_t cost = 0;  // padding entries: cost 0 and an index past every pair
