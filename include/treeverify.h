@@ -130,8 +130,12 @@ int tree_build_index(const int32_t* parent, const int32_t* cu_nodes, int32_t bat
  *   out          [total_nodes, hq, head_dim], dtype
  *   lse          [total_nodes, hq] float or NULL
  *   workspace    device scratch of >= tree_verify_attention_workspace_size(...) bytes
- *                (may be NULL when that size is 0); no initial contents are needed.
- *                Calls that share one workspace must not overlap.
+ *                (may be NULL when that size is 0).  Zero-fill it once before its
+ *                first use: its first 2048 bytes hold counters (finish tickets of
+ *                work items whose partial results are merged inside the kernel,
+ *                queue heads of a launch that schedules its own work items), and
+ *                every call leaves them zero again.  Calls that share one
+ *                workspace must not overlap.
  *   err          TV_ERR_BLOCK, TV_ERR_TOO_MANY_NODES
  */
 size_t tree_verify_attention_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,

@@ -87,22 +87,24 @@ def test_attention_host_checks(lib):
     # compute unit needs none either
     assert lib.tree_verify_attention_workspace_size(1, 15, 15, 128, 4, 4, 64, tv.TV_DTYPE_F32) == 0
     assert lib.tree_verify_attention_workspace_size(4, 1024, 256, 32768, 64, 8, 128, tv.TV_DTYPE_BF16) == 0
-    # more long items than compute units run persistently: 8 queue heads (one per die),
-    # then (256-byte aligned) the pair order; 512 pairs x 2 row tiles fill every die's
-    # last round, so nothing is cut
+    # every workspace starts with 2048 bytes of counter words (zero between calls)
+    counters = 2048
+    # more long items than compute units run persistently (queue heads in the counter
+    # words), then the pair order; 512 pairs x 2 row tiles fill every die's last round,
+    # so nothing is cut
     assert lib.tree_verify_attention_workspace_size(64, 5000, 96, 4096, 32, 8, 128,
-                                                    tv.TV_DTYPE_BF16) == 256 + 512 * 4
+                                                    tv.TV_DTYPE_BF16) == counters + 512 * 4
     # 64 pairs x 10 row tiles = 80 items per die of 32 compute units: the 16 items of the
-    # last round are cut in 2 pieces, each with a 256-row partial (128 fp32 outputs + 1
-    # log-sum-exp per row); then 8 queue heads and one finish ticket per cut item, then
-    # the pair order
+    # last round are cut in 2 pieces, each with a 256-row partial (128 fp32 outputs, then
+    # 1 log-sum-exp per row); then the pair order
     rows = 8 * 16 * 2 * 256
-    tail = rows * 128 * 4 + rows * 4
-    counters_end = tail + (8 + 8 * 16) * 4
-    order_off = (counters_end + 255) // 256 * 256
-    assert tail % 256 == 0
+    lse_off = counters + rows * 128 * 4
+    assert lse_off % 256 == 0 and (lse_off + rows * 4) % 256 == 0
     assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128,
-                                                    tv.TV_DTYPE_BF16) == order_off + 64 * 4
+                                                    tv.TV_DTYPE_BF16) == lse_off + rows * 4 + 64 * 4
+    # a single short verify: 32 pairs x 5 prefix splits of 64 rows
+    rows = 5 * 64 * 32
+    assert need == counters + rows * 128 * 4 + rows * 4
 
 
 def fp8_call(lib, **kw):
@@ -126,7 +128,9 @@ def test_fp8_attention_host_checks(lib):
     # the FP8 cache runs the register-staged kernel: split partials, never a pair order
     rows = 64 * 32
     need = lib.tree_verify_attention_fp8kv_workspace_size(1, 64, 64, 1088, 32, 32)
-    assert need == ((5 * rows * 128 * 4 + 255) & ~255) + 5 * rows * 4   # 5 splits of 4 blocks
+    # 2048 bytes of counter words first (every attention workspace keeps them), then
+    # 5 splits of 4 blocks
+    assert need == 2048 + 5 * rows * 128 * 4 + 5 * rows * 4
     assert lib.tree_verify_attention_fp8kv_workspace_size(8, 4672, 584, 4096, 32, 8) == 0
     assert fp8_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
                     ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE

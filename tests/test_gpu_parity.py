@@ -157,6 +157,48 @@ def test_attention_tail_pieces(gpu_lib, name):
     assert torch.equal(out, again)
 
 
+COUNTER_CASES = {
+    # 16 prefix splits merged in the kernel (tickets)
+    "splits16": ([W.tree_random(np.random.default_rng(9), 200, 8)], [8000], 8, 2),
+    # persistent launch with tail pieces (queue heads, exit count, tickets)
+    "persistent_tail": TAIL_CASES["pieces2"][:4],
+    # persistent launch, every die's last round full (queue heads only)
+    "persistent": ([W.tree_random(np.random.default_rng(30 + b), 90, 8) for b in range(64)],
+                   [512 + 57 * b for b in range(64)], 32, 8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COUNTER_CASES))
+def test_attention_workspace_counters_left_zero(gpu_lib, name):
+    """The workspace's counter words are zero after every call, so one zero-filled
+    workspace serves any number of calls; the outputs of repeated calls are identical."""
+    parents, plens, hq, hkv = COUNTER_CASES[name]
+    case = W.make_case(name, parents, plens, hq, hkv, 128, W.DT_BF16, 10, 23, with_probs=False)
+    dev = W.case_to_device(case, probs=False)
+    mn = max(1, case.max_nodes)
+    anc, _, _, _ = gpu_index(gpu_lib, case, dev)
+    need = gpu_lib.tree_verify_attention_workspace_size(case.batch, case.total_nodes, mn,
+                                                        case.max_prefix, hq, hkv, 128,
+                                                        gpu_lib.TV_DTYPE_BF16)
+    assert need > 2048
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out, lse, err = gpu_lib.tree_verify_attention(
+            dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"], dev["prefix_len"],
+            dev["k_tree"], dev["v_tree"], dev["cu_nodes"], anc, mn, case.max_prefix, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert int(ws[:2048].count_nonzero().item()) == 0
+        outs.append((out.clone(), lse.clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    nodes = sample_nodes(case, 6, seed=3)
+    want, want_lse = oracle_attention(case, nodes)
+    rows = rows_of(case, nodes)
+    assert np.abs(to_f64(outs[0][0])[rows] - want[rows]).max() <= TOL_BF16
+
+
 def test_attention_aliased_block_tables(gpu_lib):
     parents = [W.tree_kary_levels(3, 3)] * 4
     case = W.make_case("alias", parents, [700] * 4, 8, 2, 128, W.DT_BF16, 10, 3, alias_prefix=True,

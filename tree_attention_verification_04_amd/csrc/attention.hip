@@ -25,8 +25,8 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   p.total_work = 0;
   p.tail_pieces = 1;
   p.persistent = false;
+  p.merge_in_kernel = false;
   p.die_slots = 0;
-  p.n_counters = 0;
   p.workspace = 0;
   if (!p.mfma || batch <= 0 || hkv <= 0) return p;
   const int group = hq / hkv;
@@ -75,25 +75,22 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
       p.die_slots = p.tail_whole + tail * k;
     }
   }
-  // the ordering kernel also clears the queue heads and tickets (no launch of its own)
   if (p.persistent && pairs <= kMaxOrderedPairs) p.ordered = true;
-  size_t ws = 0;
-  if (p.splits > 1) {
-    const size_t rows = static_cast<size_t>(total_nodes) * hq;
-    const size_t o_bytes = static_cast<size_t>(p.splits) * rows * head_dim * sizeof(float);
-    const size_t l_bytes = static_cast<size_t>(p.splits) * rows * sizeof(float);
-    ws = ((o_bytes + 255) & ~static_cast<size_t>(255)) + l_bytes;
-  }
-  if (p.tail_pieces > 1) {  // partials [8 * tail_items * pieces * 256 rows] (out, lse)
-    const size_t prow = static_cast<size_t>(kXCDs) * p.tail_items * p.tail_pieces * kMfmaRowsPerWG;
-    ws = ((prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)) +
-         prow * sizeof(float);
-  }
-  p.n_counters = 0;
-  if (p.persistent) {  // 8 queue heads, then one finish ticket per tail item
-    p.n_counters = kXCDs + kXCDs * p.tail_items;
-    p.counters_off = (ws + 255) & ~static_cast<size_t>(255);
-    ws = p.counters_off + static_cast<size_t>(p.n_counters) * sizeof(int);
+  // Workspace: [counter words, kCounterBytes] [partial outputs] [partial lse] [pair
+  // order].  The counter words are zero between calls: every call that uses them
+  // (tickets of the in-kernel split merge, queue heads of a persistent launch)
+  // leaves them zero again, so the caller zero-fills a new workspace once.
+  size_t prow = 0;  // partial rows
+  if (p.splits > 1) prow = static_cast<size_t>(p.splits) * total_nodes * hq;
+  if (p.tail_pieces > 1)
+    prow = static_cast<size_t>(kXCDs) * p.tail_items * p.tail_pieces * kMfmaRowsPerWG;
+  p.merge_in_kernel = p.tail_pieces > 1;  // at most 8 * 31 tickets (< kMaxTickets)
+  // every plan with a workspace keeps the counter words first, whether it uses them
+  size_t ws = prow > 0 || p.persistent || p.ordered ? kCounterBytes : 0;
+  p.part_off = ws;
+  if (prow > 0) {
+    p.lse_off = (p.part_off + prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    ws = p.lse_off + prow * sizeof(float);
   }
   if (p.ordered) {
     p.order_off = (ws + 255) & ~static_cast<size_t>(255);
@@ -225,30 +222,17 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
   a.blocks_per_split = plan.blocks_per_split;
   a.row_tiles = plan.row_tiles;
   a.total_work = static_cast<int>(plan.total_work);
-  if (plan.splits > 1) {
-    const size_t rows = static_cast<size_t>(total_nodes) * hq;
-    const size_t o_bytes = static_cast<size_t>(plan.splits) * rows * head_dim * sizeof(float);
-    a.part_o = static_cast<float*>(workspace);
-    const size_t o_pad = (o_bytes + 255) & ~static_cast<size_t>(255);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_pad);
-  }
   a.tail_pieces = plan.tail_pieces;
   a.tail_whole = plan.tail_whole;
   a.tail_items = plan.tail_items;
   a.die_slots = plan.die_slots;
-  if (plan.tail_pieces > 1) {
-    const size_t prow =
-        static_cast<size_t>(tv::kXCDs) * plan.tail_items * plan.tail_pieces * tv::kMfmaRowsPerWG;
-    a.part_o = static_cast<float*>(workspace);
-    const size_t o_pad = (prow * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_pad);
+  char* wsb = static_cast<char*>(workspace);
+  if (plan.splits > 1 || plan.tail_pieces > 1) {
+    a.part_o = reinterpret_cast<float*>(wsb + plan.part_off);
+    a.part_lse = reinterpret_cast<float*>(wsb + plan.lse_off);
   }
-  if (plan.persistent) {
-    a.counters = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.counters_off);
-    a.n_counters = plan.n_counters;
-    a.queue = a.counters;
-    a.tail_cnt = a.counters + tv::kXCDs;
-  }
+  if (plan.persistent) a.queue = reinterpret_cast<int*>(wsb) + tv::kQueueWord;
+  if (plan.merge_in_kernel) a.tickets = reinterpret_cast<int*>(wsb) + tv::kTicketWord;
   auto s = static_cast<hipStream_t>(stream);
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
   if (plan.ordered) {

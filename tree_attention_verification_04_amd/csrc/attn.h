@@ -24,9 +24,8 @@ struct AttnArgs {
   const int* pair_order;    // [batch * hkv] (sequence, KV head) pairs, longest first; or null
   const float* k_scale;     // FP8 prefix cache: [num_blocks, hkv, 64] scales; null for bf16
   const float* v_scale;
-  int* counters;            // persistent launch: [n_counters] words the launch zeroes first
-  int* queue;               // = counters: [8] queue heads, one per die
-  int* tail_cnt;            // = counters + 8: [8 * tail_items] finish tickets of the tail items
+  int* queue;               // persistent launch: [8] queue heads (one per die), exit count
+  int* tickets;             // in-kernel merge: one finish ticket per cut work item
   int words, batch, total_nodes, total_rows, max_nodes, max_prefix;
   int num_blocks, max_blocks, hq, hkv, group;
   int splits, blocks_per_split, row_tiles, total_work;
@@ -35,7 +34,6 @@ struct AttnArgs {
   // prefix ranges each, merged by the piece that finishes last (1 = off)
   int tail_pieces, tail_whole, tail_items;
   int die_slots;            // queue slots per die (persistent launch)
-  int n_counters;
   float scale;              // softmax scale (natural-exp units)
 };
 
@@ -84,15 +82,20 @@ struct AttnPlan {
   int row_tiles;      // row tiles per (sequence, kv head)
   long total_work;    // workgroups with work
   bool persistent;    // long items over several rounds: one workgroup per CU pulls items
+  bool merge_in_kernel;  // cut items merged by the piece that finishes last (no combine pass)
   int die_slots;      // queue slots per die
   int tail_pieces;    // tail balancing: pieces per tail item (1 = off)
   int tail_whole;     // per die: work items that run whole
   int tail_items;     // per die: work items cut into tail_pieces pieces
-  int n_counters;     // queue heads + tail tickets
-  size_t workspace;   // bytes of split or tail partials, counters and the pair order
-  size_t order_off;   // workspace offset of the pair order
-  size_t counters_off;  // workspace offset of the counters (partials start at 0)
+  size_t workspace;   // bytes: counter words, partials, pair order
+  size_t part_off, lse_off, order_off;  // workspace offsets
 };
+
+// Counter words at the start of the workspace (zero between calls).
+constexpr int kCounterBytes = 2048;
+constexpr int kQueueWord = 0;        // [8] queue heads, [8] exit count of a persistent launch
+constexpr int kTicketWord = 16;      // finish tickets from here
+constexpr int kMaxTickets = kCounterBytes / 4 - kTicketWord;
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
                         int head_dim, int dtype, bool fp8_kv);

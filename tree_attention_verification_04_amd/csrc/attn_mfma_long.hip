@@ -42,6 +42,7 @@ constexpr int kWavesL = 8;
 constexpr int kTL = 64 * kWavesL;
 constexpr float kLazy = 8.0f;         // log2 of the largest unnormalised probability
 constexpr int kRing = 4;              // slots of the K, V and ancestor rings
+constexpr int kMaxPieces = kMaxTailPieces;  // tail pieces of one work item
 constexpr int kVOff = kRing * kTileBytes;
 constexpr int kAncSlotBytes = kMfmaRowsPerWG * 8;  // per wavefront: 32 low, 32 high words
 constexpr int kAncOffL = kVOff + kRing * kTileBytes;
@@ -511,16 +512,21 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
   float lse = l_tot > 0.0f ? m_out * a.scale + logf(l_tot) : -INFINITY;
   if (pieces > 1) {
     // a piece of a tail item: store the piece's normalised output and log-sum-exp,
-    // then take a ticket; the piece that takes the last one merges all pieces.  The
-    // others' stores are visible to it: every lane's stores complete before the
-    // barrier, one thread then releases them at device scope (the die's L2 is written
-    // back) and takes the ticket; the merging piece's ticket thread acquires (caches
-    // invalidated) before the barrier that starts the merge.  One fence per workgroup
-    // rather than per lane: each fence writes back or invalidates the whole L2 of the
-    // die, which the other work items of the pair are reading their K/V tiles from.
+    // then take a ticket; the piece that takes the last one merges all pieces and
+    // zeroes the ticket for the next call.  The others' stores are visible to it:
+    // every lane's stores complete before the barrier, one thread then releases them
+    // at device scope (the die's L2 is written back) and takes the ticket; the
+    // merging piece's ticket thread acquires (caches invalidated) before the barrier
+    // that starts the merge.  One fence per workgroup rather than per lane: each fence
+    // writes back or invalidates the whole L2 of the die, which the other work items
+    // of the pair are reading their K/V tiles from.  (Prefix splits of a short verify
+    // are merged by k_attn_combine instead: there every workgroup runs at once and
+    // such fences, one per workgroup, made the call slower than the extra launch.)
     const long p_base = static_cast<long>(tail_slot) * pieces * kMfmaRowsPerWG + rl;
+    const long p_stride = kMfmaRowsPerWG;
+    const int ticket = tail_slot, n_pieces = pieces, my_piece = piece;
     if (row_ok) {
-      float* po = a.part_o + (p_base + static_cast<long>(piece) * kMfmaRowsPerWG) * kD;
+      float* po = a.part_o + (p_base + my_piece * p_stride) * kD;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -528,25 +534,27 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
           *reinterpret_cast<float4*>(po + 32 * dt + 8 * qd + 4 * half) =
               make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv,
                           acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv);
-      if (half == 0) a.part_lse[p_base + static_cast<long>(piece) * kMfmaRowsPerWG] = lse;
+      if (half == 0) a.part_lse[p_base + my_piece * p_stride] = lse;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     int* s_last = reinterpret_cast<int*>(smem + kMaskOff + 4);
     if (tid == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      *s_last = atomicAdd(a.tail_cnt + tail_slot, 1) == pieces - 1;
+      const bool last = atomicAdd(a.tickets + ticket, 1) == n_pieces - 1;
+      if (last) a.tickets[ticket] = 0;  // every piece has taken its ticket
+      *s_last = last;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (*s_last == 0) return;
     if (!row_ok) return;
     // lse = log sum_p exp(lse_p), out = sum_p exp(lse_p - lse) out_p
-    float lp[kMaxTailPieces];
+    float lp[kMaxPieces];
     float mx = -INFINITY;
 #pragma unroll
-    for (int pc = 0; pc < kMaxTailPieces; ++pc) {
-      lp[pc] = pc < pieces ? a.part_lse[p_base + static_cast<long>(pc) * kMfmaRowsPerWG] : -INFINITY;
+    for (int pc = 0; pc < kMaxPieces; ++pc) {
+      lp[pc] = pc < n_pieces ? a.part_lse[p_base + pc * p_stride] : -INFINITY;
       mx = fmaxf(mx, lp[pc]);
     }
     const float mref = mx == -INFINITY ? 0.0f : mx;
@@ -554,11 +562,11 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16_t{};
     float w_sum = 0.0f;
 #pragma unroll
-    for (int pc = 0; pc < kMaxTailPieces; ++pc) {
-      if (pc >= pieces) break;
+    for (int pc = 0; pc < kMaxPieces; ++pc) {
+      if (pc >= n_pieces) break;
       const float w = __builtin_amdgcn_exp2f((lp[pc] - mref) * kLog2e);
       w_sum += w;
-      const float* po = a.part_o + (p_base + static_cast<long>(pc) * kMfmaRowsPerWG) * kD;
+      const float* po = a.part_o + (p_base + pc * p_stride) * kD;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -574,31 +582,29 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     lse = w_sum > 0.0f ? mx + logf(w_sum) : -INFINITY;
   }
   if (!row_ok) return;
-  if (a.splits == 1) {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + grow * kD;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d = 32 * dt + 8 * qd + 4 * half;
-        *reinterpret_cast<uint2*>(out + d) =
-            make_uint2(pack2_bf16(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv),
-                       pack2_bf16(acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv));
-      }
-    if (a.lse != nullptr && half == 0) a.lse[grow] = lse;
-  } else {
+  if (a.splits > 1) {  // k_attn_combine merges the prefix splits after the kernel ends
     float* po = a.part_o + (static_cast<long>(split) * a.total_rows + grow) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int d = 32 * dt + 8 * qd + 4 * half;
-        *reinterpret_cast<float4*>(po + d) =
-            make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv, acc[dt][4 * qd + 2] * inv,
-                        acc[dt][4 * qd + 3] * inv);
-      }
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * qd + 4 * half) =
+            make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv,
+                        acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv);
     if (half == 0) a.part_lse[static_cast<long>(split) * a.total_rows + grow] = lse;
+    return;
   }
+  uint16_t* out = static_cast<uint16_t*>(a.out) + grow * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d = 32 * dt + 8 * qd + 4 * half;
+      *reinterpret_cast<uint2*>(out + d) =
+          make_uint2(pack2_bf16(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv),
+                     pack2_bf16(acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv));
+    }
+  if (a.lse != nullptr && half == 0) a.lse[grow] = lse;
 }
 
 // Without a queue, workgroup i runs slot i / 8 of die i % 8's list (the hardware
@@ -620,7 +626,7 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
       __syncthreads();
       k_slot = *s_pull;
       __syncthreads();  // every lane has read the slot before lane 0 takes the next
-      if (k_slot >= a.die_slots) {
+      if (k_slot < 0 || k_slot >= a.die_slots) {
         if (++tried == kXCDs) break;
         die = (die + 1) & (kXCDs - 1);
         continue;
@@ -636,13 +642,15 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
     long_item(item_args, die, k_slot);
     if (!queued) break;
   }
-}
-
-// zero n words (the counters of a persistent launch; a kernel rather than a memset,
-// so that the launch can be captured in a graph)
-__global__ void __launch_bounds__(256) k_clear_words(int* p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
+  // the last workgroup to finish zeroes the queue heads and the exit count for the
+  // next call (every other workgroup has taken its last slot before counting itself)
+  if (queued && threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (atomicAdd(a.queue + kXCDs, 1) == static_cast<int>(gridDim.x) - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int d = 0; d <= kXCDs; ++d) a.queue[d] = 0;
+    }
+  }
 }
 
 int launch_attn_long(const AttnArgs& a, hipStream_t s) {
@@ -652,24 +660,14 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
     attr_set = true;
   }
-  int grid = 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
-  if (a.queue != nullptr) {
-    if (a.pair_order == nullptr) {  // else the ordering kernel has cleared the counters
-      hipLaunchKernelGGL(k_clear_words, dim3(ceil_div(a.n_counters, 256)), dim3(256), 0, s,
-                         a.counters, a.n_counters);
-      const int st = check_launch("tree_verify_attention/counters");
-      if (st != TV_OK) return st;
-    }
-    grid = kCUs;
-  }
+  const int grid = a.queue != nullptr ? kCUs : 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
   hipLaunchKernelGGL(k_attn_long, dim3(grid), dim3(kTL), kSmemL, s, a);
   const int st = check_launch("tree_verify_attention/long");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);
 }
 
-// ---- dispatch order of the long work items (and, for a persistent launch, the
-// clear of its queue heads and finish tickets): the (sequence, KV head) pairs
+// ---- dispatch order of the long work items: the (sequence, KV head) pairs
 // ranked by estimated cost, largest first (longest-processing-time-first list
 // scheduling: each free compute unit takes the next item of its die's list).
 // Cost of a pair = its tiles x its live 64-row units summed over its row tiles, from
@@ -678,8 +676,6 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
 __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
   __shared__ __attribute__((aligned(16))) uint32_t s_cost[kMaxOrderedPairs];
   const int pairs = a.batch * a.hkv;
-  if (a.counters != nullptr)  // queue heads and tail tickets of a persistent launch start at zero
-    for (int i = threadIdx.x; i < a.n_counters; i += 1024) a.counters[i] = 0;
   const int padded = (pairs + 3) & ~3;
   for (int p = threadIdx.x; p < padded; p += 1024) {
     uint32_t cost = 0;  // padding entries: cost 0 and an index past every pair
