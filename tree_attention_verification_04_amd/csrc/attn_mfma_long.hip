@@ -622,6 +622,8 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   int k_slot = blockIdx.x / kXCDs, tried = 0;
   for (;;) {  // one call site of the item body (register pressure)
     if (queued) {
+      // a slot is taken only when this workgroup is free (taking the next one ahead,
+      // while an item runs, reserves work for a busy unit: serving-64 267 -> 320 us)
       if (threadIdx.x == 0) *s_pull = atomicAdd(a.queue + die, 1);
       __syncthreads();
       k_slot = *s_pull;
@@ -671,14 +673,17 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
 // ranked by estimated cost, largest first (longest-processing-time-first list
 // scheduling: each free compute unit takes the next item of its die's list).
 // Cost of a pair = its tiles x its live 64-row units summed over its row tiles, from
-// the same clamped lengths the attention kernel uses.  One workgroup; rank of pair i
-// = number of pairs with a larger cost, or an equal cost and a smaller index.
+// the same clamped lengths the attention kernel uses.  One workgroup sorts the pairs
+// by cost, larger first, equal costs in index order.
 __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_cost[kMaxOrderedPairs];
+  // key of pair p = cost << 32 | ~p: sorted descending, larger costs come first and
+  // equal costs in index order; padding keys are 0 and sort last
+  __shared__ uint64_t s_key[kMaxOrderedPairs];
   const int pairs = a.batch * a.hkv;
-  const int padded = (pairs + 3) & ~3;
-  for (int p = threadIdx.x; p < padded; p += 1024) {
-    uint32_t cost = 0;  // padding entries: cost 0 and an index past every pair
+  int n2 = 2;
+  while (n2 < pairs) n2 <<= 1;
+  for (int p = threadIdx.x; p < n2; p += 1024) {
+    uint64_t key = 0;
     if (p < pairs) {
       const int b = p / a.hkv;
       const int n0 = a.cu_nodes[b];
@@ -691,26 +696,32 @@ __global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
         const int live = rows - t * kMfmaRowsPerWG;
         if (live > 0) units += (min(live, kMfmaRowsPerWG) + 63) / 64;
       }
-      cost = static_cast<uint32_t>(tiles * units);
+      const uint32_t cost = static_cast<uint32_t>(tiles) * static_cast<uint32_t>(units);
+      key = (static_cast<uint64_t>(cost) << 32) | static_cast<uint32_t>(~p);
     }
-    s_cost[p] = cost;
+    s_key[p] = key;
   }
   __syncthreads();
-  // one thread per pair: its rank is the number of pairs that come first (larger
-  // cost, or equal cost and smaller index); every thread reads the same four
-  // costs at a time (an LDS broadcast)
-  for (int i = threadIdx.x; i < pairs; i += 1024) {
-    const uint32_t ci = s_cost[i];
-    int rank = 0;
-    for (int j = 0; j < padded; j += 4) {
-      const uint4 c = *reinterpret_cast<const uint4*>(&s_cost[j]);
-      rank += (c.x > ci) || (c.x == ci && j < i);
-      rank += (c.y > ci) || (c.y == ci && j + 1 < i);
-      rank += (c.z > ci) || (c.z == ci && j + 2 < i);
-      rank += (c.w > ci) || (c.w == ci && j + 3 < i);
+  // bitonic sort, descending: blocks of size k merged by compare-exchange at
+  // distance j (log2(n2) (log2(n2) + 1) / 2 steps, one barrier each)
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 1024) {
+        const int partner = i ^ j;
+        if (partner > i) {
+          const uint64_t x = s_key[i], y = s_key[partner];
+          const bool descending = (i & k) == 0;
+          if (descending ? x < y : x > y) {
+            s_key[i] = y;
+            s_key[partner] = x;
+          }
+        }
+      }
+      __syncthreads();
     }
-    order[rank] = i;
   }
+  for (int i = threadIdx.x; i < pairs; i += 1024)
+    order[i] = static_cast<int>(~static_cast<uint32_t>(s_key[i]));
 }
 
 int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s) {
