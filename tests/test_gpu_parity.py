@@ -274,6 +274,21 @@ def test_accept_exhaustive_patterns_batched(gpu_lib):
     assert_accept_equal(gpu_accept(gpu_lib, case, dev, n), oracle_accept(case, n))
 
 
+@pytest.mark.parametrize("vocab", [65537, 70002, 131072])
+def test_accept_large_vocab_bitexact(gpu_lib, vocab):
+    """Vocabularies past the one-kernel limit: residual sums per 4096-entry chunk (whole
+    chunks by 16-byte loads when rows are 16-byte aligned, else element by element),
+    then the chunk and the element; rows with mostly equal probabilities put the
+    rejection point deep in the trees."""
+    parents = [W.tree_random(np.random.default_rng(40 + b), n, 5) for b, n in enumerate([9, 1, 30])]
+    case = W.make_case("bigv", parents, [0, 0, 0], 1, 1, 64, W.DT_F32, vocab, 31)
+    rng = np.random.default_rng(vocab)
+    same = rng.random(case.total_nodes) < 0.6
+    case.p_target[same] = case.p_draft[same]
+    dev = W.case_to_device(case)
+    assert_accept_equal(gpu_accept(gpu_lib, case, dev, 8), oracle_accept(case, 8))
+
+
 def test_accept_error_words(gpu_lib):
     case = W.make_case("err", [W.tree_chain(3), W.tree_heap(7), W.tree_chain(4)], [0, 0, 0], 1, 1,
                        64, W.DT_F32, 50, 9)

@@ -30,6 +30,9 @@ constexpr int kAcceptThreads = 256;
 constexpr int kResidChunk = 4096;                       // vocabulary entries per chunk
 constexpr int kResidPerThread = kResidChunk / kAcceptThreads;
 constexpr int kFusedVocab = 65536;  // up to this vocabulary the walk's workgroup resamples
+constexpr int kMaxVocab = 1 << 18;
+constexpr int kMaxResidChunks = kMaxVocab / kResidChunk;
+static_assert(kResidPerThread % 4 == 0, "whole float4 per thread");
 
 #pragma clang fp contract(off)
 
@@ -284,10 +287,32 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_partial(
   const int k0 = chunk * kResidChunk;
   const int k1 = min(vocab, k0 + kResidChunk);
   uint64_t sr = 0, st = 0;
-  for (int k = k0 + threadIdx.x; k < k1; k += kAcceptThreads) {
-    const float t = pt[row + k];
-    sr += resid_weight(t, pd[row + k]);
-    st += target_weight(t);
+  const bool aligned =
+      ((vocab & 3) | ((reinterpret_cast<uintptr_t>(pt) | reinterpret_cast<uintptr_t>(pd)) & 15)) == 0;
+  if (aligned && k1 - k0 == kResidChunk) {
+    // whole chunk, rows 16-byte aligned: each thread takes 4 float4 of each row,
+    // all 8 loads in flight at once
+    const float4* t4 = reinterpret_cast<const float4*>(pt + row + k0);
+    const float4* d4 = reinterpret_cast<const float4*>(pd + row + k0);
+    float4 tv[kResidPerThread / 4], dv[kResidPerThread / 4];
+#pragma unroll
+    for (int j = 0; j < kResidPerThread / 4; ++j) {
+      tv[j] = t4[threadIdx.x + j * kAcceptThreads];
+      dv[j] = d4[threadIdx.x + j * kAcceptThreads];
+    }
+#pragma unroll
+    for (int j = 0; j < kResidPerThread / 4; ++j) {
+      sr += resid_weight(tv[j].x, dv[j].x) + resid_weight(tv[j].y, dv[j].y) +
+            resid_weight(tv[j].z, dv[j].z) + resid_weight(tv[j].w, dv[j].w);
+      st += target_weight(tv[j].x) + target_weight(tv[j].y) + target_weight(tv[j].z) +
+            target_weight(tv[j].w);
+    }
+  } else {
+    for (int k = k0 + threadIdx.x; k < k1; k += kAcceptThreads) {
+      const float t = pt[row + k];
+      sr += resid_weight(t, pd[row + k]);
+      st += target_weight(t);
+    }
   }
   sr = block_sum_u64(sr);
   st = block_sum_u64(st);
@@ -304,16 +329,20 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
     int32_t* __restrict__ err) {
   __shared__ int s_mode, s_chunk;
   __shared__ uint64_t s_rem;
+  __shared__ uint64_t s_part[2 * kMaxResidChunks];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int c = ws_c[b];
   if (c < 0) return;
   const int n0 = cu_nodes[b];
   const uint64_t* mine = part + static_cast<long>(b) * chunks * 2;
+  // the per-chunk sums, loaded by all threads at once, then scanned from LDS
+  for (int k = tid; k < 2 * chunks; k += kAcceptThreads) s_part[k] = mine[k];
+  __syncthreads();
   if (tid == 0) {
     uint64_t zr = 0, zt = 0;
     for (int k = 0; k < chunks; ++k) {
-      zr += mine[2 * k];
-      zt += mine[2 * k + 1];
+      zr += s_part[2 * k];
+      zt += s_part[2 * k + 1];
     }
     const int mode = zr > 0 ? 0 : (zt > 0 ? 1 : -1);
     s_mode = mode;
@@ -322,7 +351,7 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
       uint64_t cum = 0;
       int kc = chunks - 1;
       for (int k = 0; k < chunks; ++k) {
-        const uint64_t s = mine[2 * k + mode];
+        const uint64_t s = s_part[2 * k + mode];
         if (t < cum + s) {
           kc = k;
           break;
@@ -379,7 +408,7 @@ extern "C" int tree_accept(const float* p_target, const float* p_draft, const in
   tv::clear_error();
   if (batch < 0 || total_nodes < 0 || max_path < 0)
     return tv::fail(TV_EINVAL, "tree_accept: negative size");
-  if (vocab <= 0 || vocab > (1 << 18))
+  if (vocab <= 0 || vocab > tv::kMaxVocab)
     return tv::fail(TV_EUNSUPPORTED, "tree_accept: vocab must be in [1, 262144]");
   if (max_nodes < 1 || max_nodes > TV_MAX_NODES)
     return tv::fail(TV_EUNSUPPORTED, "tree_accept: max_nodes must be in [1, 2048]");
