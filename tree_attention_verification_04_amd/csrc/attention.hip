@@ -59,13 +59,17 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   p.tail_pieces = 1;
   p.tail_whole = 0;
   p.tail_items = 0;
-  const long per_die = ceil_div(static_cast<int>(pairs), kXCDs) * static_cast<long>(p.row_tiles) *
-                       p.splits;
+  // (the pipelined kernel deals pairs to dies, pair r to die r % 8; the staged
+  // kernel deals each die a contiguous range of work indices)
+  const long per_die =
+      p.long_items ? ceil_div(static_cast<int>(pairs), kXCDs) * static_cast<long>(p.row_tiles) *
+                         p.splits
+                   : (p.total_work + kXCDs - 1) / kXCDs;
   p.die_slots = per_die <= INT32_MAX / kMaxTailPieces ? static_cast<int>(per_die) : 0;
-  p.persistent = p.long_items && p.die_slots > kCUsPerXCD;
+  p.persistent = p.die_slots > kCUsPerXCD;
   // tail balancing: when a die's items do not fill its last round evenly, the items
   // of that round are cut into prefix pieces, so the last round ends sooner
-  if (p.persistent && p.splits == 1) {
+  if (p.persistent && p.long_items && p.splits == 1) {
     const int tail = p.die_slots % kCUsPerXCD;
     const int k = tail_pieces_for(tail, kCUsPerXCD);
     if (k > 1) {
@@ -75,7 +79,7 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
       p.die_slots = p.tail_whole + tail * k;
     }
   }
-  if (p.persistent && pairs <= kMaxOrderedPairs) p.ordered = true;
+  if (p.persistent && p.long_items && pairs <= kMaxOrderedPairs) p.ordered = true;
   // Workspace: [counter words, kCounterBytes] [partial outputs] [partial lse] [pair
   // order].  The counter words are zero between calls: every call that uses them
   // (tickets of the in-kernel split merge, queue heads of a persistent launch)

@@ -124,4 +124,57 @@ constexpr int kLongMinTiles = TV_LONG_MIN_TILES;
 constexpr int kMinSplitBlocks = 4;   // prefix blocks per split at least (when splitting)
 constexpr int kMaxOrderedPairs = 2048;  // pairs the ordering kernel ranks in one workgroup
 
+// Work items of a tree-attention launch.  Without a queue, workgroup i runs slot
+// i / 8 of die i % 8's list (the hardware hands workgroups to dies round-robin in
+// launch order).  With one (items over several rounds), one workgroup per compute
+// unit takes slots from the queue of the die it runs on (the hardware die id) until
+// it is empty, then from the other dies' queues: no unit idles while another die's
+// dispatch waits, and no workgroup ever waits for another.  A slot is taken only
+// when the workgroup is free (taking the next one ahead, while an item runs,
+// reserves work for a busy unit: serving-64 267 -> 320 us).  s_pull is one LDS word.
+// kQueued false: the plain mapping only (no loop, so the item body keeps the
+// registers it would have as a kernel of its own).
+template <bool kQueued, class Item>
+__device__ __forceinline__ void run_work_items(const AttnArgs& a, int* s_pull, Item item) {
+  if constexpr (!kQueued) {
+    item(a, static_cast<int>(blockIdx.x % kXCDs), static_cast<int>(blockIdx.x / kXCDs));
+    return;
+  }
+  const bool queued = true;
+  const int home = static_cast<int>(__builtin_amdgcn_s_getreg(20 | (3 << 11))) & (kXCDs - 1);
+  int die = queued ? home : static_cast<int>(blockIdx.x % kXCDs);
+  int k_slot = blockIdx.x / kXCDs, tried = 0;
+  for (;;) {  // one call site of the item body (register pressure)
+    if (queued) {
+      if (threadIdx.x == 0) *s_pull = atomicAdd(a.queue + die, 1);
+      __syncthreads();
+      k_slot = *s_pull;
+      __syncthreads();  // every lane has read the slot before lane 0 takes the next
+      if (k_slot < 0 || k_slot >= a.die_slots) {
+        if (++tried == kXCDs) break;
+        die = (die + 1) & (kXCDs - 1);
+        continue;
+      }
+    }
+    // the item body reads its arguments afresh from the kernel-argument segment (the
+    // pointer is opaque to the compiler), so that no argument stays in a scalar
+    // register across items: the body alone needs nearly all of them
+    const __attribute__((address_space(4))) char* ap =
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    const AttnArgs item_args = *(const AttnArgs*)ap;
+    item(item_args, die, k_slot);
+    if (!queued) break;
+  }
+  // the last workgroup to finish zeroes the queue heads and the exit count for the
+  // next call (every other workgroup has taken its last slot before counting itself)
+  if (queued && threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (atomicAdd(a.queue + kXCDs, 1) == static_cast<int>(gridDim.x) - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int d = 0; d <= kXCDs; ++d) a.queue[d] = 0;
+    }
+  }
+}
+
 }  // namespace tv

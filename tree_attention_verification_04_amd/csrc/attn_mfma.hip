@@ -47,7 +47,7 @@ using TileRegs = TileRegsT<kThreads>;
 // head, position); its tiles are dequantized to bf16 on their way into LDS and
 // everything after that is the bf16 kernel.
 template <bool kFp8>
-__global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
+__device__ __forceinline__ void mfma_item(const AttnArgs& a, const int die, const int k_slot) {
   auto load_tile = [](const TileSrc& src, int tid, TileRegs& r) __attribute__((always_inline)) {
     load_tile_t<kThreads, kFp8>(src, tid, r);
   };
@@ -57,9 +57,8 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kAncOff + 3 * kAncBytes);
   int* s_simd_slots = reinterpret_cast<int*>(smem + kAncOff + 3 * kAncBytes + 16);  // [4]
 
-  // ---- work item (XCD-aware: consecutive work indices share an XCD)
-  const int per_xcd = gridDim.x / 8;
-  const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // ---- work item (XCD-aware: each die runs a contiguous range of work indices)
+  const int work = die * a.die_slots + k_slot;
   if (work >= a.total_work) return;
   const int tile = work % a.row_tiles;
   const int rest = work / a.row_tiles;
@@ -498,6 +497,16 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
   if (half == 0) a.part_lse[static_cast<long>(split) * a.total_rows + grow] = lse;
 }
 
+// Work items as run_work_items hands them out (kQueued: persistent, from the queues).
+template <bool kFp8, bool kQueued>
+__global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  run_work_items<kQueued>(a, reinterpret_cast<int*>(smem + kAncOff + 3 * kAncBytes + 48),
+                 [](const AttnArgs& args, int die, int k_slot) __attribute__((always_inline)) {
+                   mfma_item<kFp8>(args, die, k_slot);
+                 });
+}
+
 // Merge of the prefix splits, one thread per (row, 4 consecutive d):
 //   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * out_s
 // All splits' values are loaded before any is used (one memory round trip); kS is
@@ -548,17 +557,24 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_mfma<false, false>),
+                          reinterpret_cast<const void*>(&k_attn_mfma<false, true>),
+                          reinterpret_cast<const void*>(&k_attn_mfma<true, false>),
+                          reinterpret_cast<const void*>(&k_attn_mfma<true, true>)};
+    for (const void* f : fns)
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
     attr_set = true;
   }
-  const int grid = 8 * ceil_div(a.total_work, 8);
-  if (a.k_scale != nullptr)
-    hipLaunchKernelGGL(k_attn_mfma<true>, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
+  const bool fp8 = a.k_scale != nullptr, queued = a.queue != nullptr;
+  const dim3 grid(queued ? kCUs : 8 * a.die_slots), block(kThreads);
+  if (fp8 && queued)
+    hipLaunchKernelGGL((k_attn_mfma<true, true>), grid, block, kSmemBytes, s, a);
+  else if (fp8)
+    hipLaunchKernelGGL((k_attn_mfma<true, false>), grid, block, kSmemBytes, s, a);
+  else if (queued)
+    hipLaunchKernelGGL((k_attn_mfma<false, true>), grid, block, kSmemBytes, s, a);
   else
-    hipLaunchKernelGGL(k_attn_mfma<false>, dim3(grid), dim3(kThreads), kSmemBytes, s, a);
+    hipLaunchKernelGGL((k_attn_mfma<false, false>), grid, block, kSmemBytes, s, a);
   const int st = check_launch("tree_verify_attention/mfma");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);

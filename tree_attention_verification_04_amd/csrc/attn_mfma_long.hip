@@ -607,63 +607,30 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
   if (a.lse != nullptr && half == 0) a.lse[grow] = lse;
 }
 
-// Without a queue, workgroup i runs slot i / 8 of die i % 8's list (the hardware
-// hands workgroups to dies round-robin in launch order).  With one (items over
-// several rounds), one workgroup per compute unit takes slots from the queue of
-// the die it runs on (the hardware die id) until it is empty, then from the other
-// dies' queues: no unit idles while another die's dispatch waits, and no
-// workgroup ever waits for another.
+// Work items as run_work_items hands them out (kQueued: persistent, from the queues).
+template <bool kQueued>
 __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* s_pull = reinterpret_cast<int*>(smem + kMaskOff + 8);
-  const bool queued = a.queue != nullptr;
-  const int home = static_cast<int>(__builtin_amdgcn_s_getreg(20 | (3 << 11))) & (kXCDs - 1);
-  int die = queued ? home : static_cast<int>(blockIdx.x % kXCDs);
-  int k_slot = blockIdx.x / kXCDs, tried = 0;
-  for (;;) {  // one call site of the item body (register pressure)
-    if (queued) {
-      // a slot is taken only when this workgroup is free (taking the next one ahead,
-      // while an item runs, reserves work for a busy unit: serving-64 267 -> 320 us)
-      if (threadIdx.x == 0) *s_pull = atomicAdd(a.queue + die, 1);
-      __syncthreads();
-      k_slot = *s_pull;
-      __syncthreads();  // every lane has read the slot before lane 0 takes the next
-      if (k_slot < 0 || k_slot >= a.die_slots) {
-        if (++tried == kXCDs) break;
-        die = (die + 1) & (kXCDs - 1);
-        continue;
-      }
-    }
-    // the item body reads its arguments afresh from the kernel-argument segment (the
-    // pointer is opaque to the compiler), so that no argument stays in a scalar
-    // register across items: the body alone needs nearly all of them
-    const __attribute__((address_space(4))) char* ap =
-        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(ap));
-    const AttnArgs item_args = *(const AttnArgs*)ap;
-    long_item(item_args, die, k_slot);
-    if (!queued) break;
-  }
-  // the last workgroup to finish zeroes the queue heads and the exit count for the
-  // next call (every other workgroup has taken its last slot before counting itself)
-  if (queued && threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (atomicAdd(a.queue + kXCDs, 1) == static_cast<int>(gridDim.x) - 1) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      for (int d = 0; d <= kXCDs; ++d) a.queue[d] = 0;
-    }
-  }
+  run_work_items<kQueued>(a, reinterpret_cast<int*>(smem + kMaskOff + 8),
+                 [](const AttnArgs& args, int die, int k_slot) __attribute__((always_inline)) {
+                   long_item(args, die, k_slot);
+                 });
 }
 
 int launch_attn_long(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_long),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_long<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_long<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
     attr_set = true;
   }
-  const int grid = a.queue != nullptr ? kCUs : 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits;
-  hipLaunchKernelGGL(k_attn_long, dim3(grid), dim3(kTL), kSmemL, s, a);
+  if (a.queue != nullptr)
+    hipLaunchKernelGGL(k_attn_long<true>, dim3(kCUs), dim3(kTL), kSmemL, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_long<false>, dim3(8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits),
+                       dim3(kTL), kSmemL, s, a);
   const int st = check_launch("tree_verify_attention/long");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);
