@@ -343,7 +343,10 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     };
 
     // online softmax state: reference max mr (raised lazily), mc = mr * c2
-    float mr = -INFINITY, mc = 0.0f;
+    // mr starts finite: the first visible key always raises it (rescale factor
+    // exp2(-huge) = 0) and a half with no visible key (mx = -inf) never does, which
+    // gives the references and factors of a start at -inf without its special cases
+    float mr = -1.0e30f, mc = mr * c2;
     const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
     // One half-step h: mask and max of the scores c of half h, then 16 MFMAs in a
@@ -365,12 +368,11 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const bool up = mr == -INFINITY ? mx != -INFINITY : (mx - mr) * c2 > kLazy;
-      const float m_new = up ? mx : mr;
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float al = up ? __builtin_amdgcn_exp2f((mr - m_use) * c2) : 1.0f;
-      mr = m_new;
-      mc = m_use * c2;
+      const bool up = (mx - mr) * c2 > kLazy;
+      const float al_up = __builtin_amdgcn_exp2f((mr - mx) * c2);
+      mr = up ? mx : mr;
+      const float al = up ? al_up : 1.0f;
+      mc = mr * c2;
 
       uint4 kr[8];
       bf16x4_t vr[8][2];
