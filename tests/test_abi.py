@@ -131,7 +131,10 @@ def test_fp8_attention_host_checks(lib):
     # 2048 bytes of counter words first (every attention workspace keeps them), then
     # 5 splits of 4 blocks
     assert need == 2048 + 5 * rows * 128 * 4 + 5 * rows * 4
-    assert lib.tree_verify_attention_fp8kv_workspace_size(8, 4672, 584, 4096, 32, 8) == 0
+    # 640 work items (80 per die) run persistently: the counter words (queue heads) only
+    assert lib.tree_verify_attention_fp8kv_workspace_size(8, 4672, 584, 4096, 32, 8) == 2048
+    # 256 items (32 per die) fill one round: no workspace
+    assert lib.tree_verify_attention_fp8kv_workspace_size(4, 1024, 256, 32768, 64, 8) == 0
     assert fp8_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
                     ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
 

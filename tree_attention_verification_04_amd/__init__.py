@@ -195,6 +195,9 @@ def tree_verify_attention(q, k_cache, v_cache, block_table, prefix_len, k_tree, 
     q [total, hq, D]; k_cache/v_cache [num_blocks, hkv, 64, D]; block_table
     [batch, max_blocks] int32; prefix_len [batch] int32; k_tree/v_tree
     [total, hkv, D]; anc from tree_build_index.  Returns (out, lse, err).
+    workspace: a uint8 device tensor of at least the queried size, zero-filled
+    before its first use (every call leaves its counter words zero again); a
+    fresh zeroed one is allocated when none is given.
     """
     lib = load()
     fdt = (torch.float32, torch.bfloat16)
