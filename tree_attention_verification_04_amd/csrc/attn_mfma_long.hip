@@ -197,6 +197,111 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       q[s] = as_bf16x8(row_ok ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0));
   }
 
+  uint32_t tree_mask = 0u;            // set by the tree-mask pass below
+  int n_tiles = n_prefix_tiles;
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc[d] = f32x16_t{};
+  float m_out = -INFINITY, l = 0.0f;
+
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  const char* kt = static_cast<const char*>(a.k_tree);
+  const char* vt = static_cast<const char*>(a.v_tree);
+  auto tile_kind = [&](int it, int& kind, int& base) __attribute__((always_inline)) {
+    if (it < n_prefix_tiles) {
+      kind = 0;
+      base = (kb0 + it) * kKT;
+    } else {
+      uint32_t m = tree_mask;
+      for (int j = it - n_prefix_tiles; j > 0; --j) m &= m - 1;
+      kind = 1;
+      base = __ffs(m) - 1;
+    }
+  };
+  const __attribute__((address_space(4))) int32_t* bt_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
+      static_cast<long>(b) * a.max_blocks;
+  // staging lanes: load j (0, 1) of wave w covers tile rows 32 j + 4 w .. +3, lane l
+  // the row 32 j + 4 w + l / 16 and LDS chunk l % 16; the ancestor load takes the
+  // low word of row 32 w + l in lanes 0-31 and the high word in lanes 32-63
+  const int lrow = 4 * wave + (lane >> 4);
+  const int kcb = (((lane & 15) ^ (lrow & 15)) << 4);        // K: chunk c at c ^ (key & 15)
+  const int vcb = (((lane & 15) ^ ((lrow & 3) << 2)) << 4);  // V: chunk c at c ^ ((key & 3) << 2)
+  const char* anc_base = reinterpret_cast<const char*>(a.anc + static_cast<long>(n0) * a.words);
+  const uint32_t anc_lane =
+      static_cast<uint32_t>(min((r0 + rl) / a.group, count - 1) * a.words * 8 + 4 * half);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_kv = lds_addr(smem) + wave_u * 1024;
+  const uint32_t lds_anc = lds_addr(smem) + kAncOffL + wave_u * 256;
+
+  // source of tile it (clamped to the last tile)
+  struct Src {
+    const char* k;
+    const char* v;
+    uint32_t o0, o1;  // byte offsets of this lane's two rows (before the chunk offset)
+    uint32_t anc;     // this lane's byte offset of the tile's ancestor dword
+  };
+  auto tile_src = [&](int it) __attribute__((always_inline)) -> Src {
+    int kind, base;
+    tile_kind(min(it, n_tiles - 1), kind, base);
+    Src s;
+    int stride, nvalid;
+    if (kind == 0) {
+      s.anc = anc_lane;
+      stride = kD * 2;
+      const int blk = bt_row[base / kKT];
+      nvalid = min(kKT, plen - base);
+      if (blk < 0 || blk >= a.num_blocks) {
+        if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
+        s.k = kc;  // block 0 stands in; the sequence is flagged
+        s.v = vc;
+        nvalid = 1;
+      } else {
+        const long off = (static_cast<long>(blk) * a.hkv + g) * kKT * kD * 2;
+        s.k = kc + off;
+        s.v = vc + off;
+      }
+    } else {
+      s.anc = anc_lane + base * 8;
+      stride = a.hkv * kD * 2;
+      const long off = (static_cast<long>(n0 + base * 64) * a.hkv + g) * kD * 2;
+      s.k = kt + off;
+      s.v = vt + off;
+      nvalid = min(64, count - base * 64);
+    }
+    s.o0 = min(lrow, nvalid - 1) * stride;
+    s.o1 = min(32 + lrow, nvalid - 1) * stride;
+    return s;
+  };
+  // the loads of one iteration: K and ancestor words of the tile of sk, V of sv
+  auto issue = [&](const Src& sk, int slot_k, const Src& sv, int slot_v)
+      __attribute__((always_inline)) {
+    issue_loads(sk.k, sk.o0 + kcb, sk.o1 + kcb, lds_kv + slot_k * kTileBytes, anc_base, sk.anc,
+                lds_anc + slot_k * kAncSlotBytes, sv.v, sv.o0 + vcb, sv.o1 + vcb,
+                lds_kv + kVOff + slot_v * kTileBytes);
+  };
+
+  // The first three tiles' loads do not depend on the tree mask when they are all
+  // prefix tiles: then they are issued before the mask pass, whose ancestor-word
+  // loads overlap them (the tiles are older than those loads, so the compiler's
+  // wait for the words also covers them).  V slot 3, read as "tile -1" by the first
+  // half-step with zero probabilities, is cleared.
+  Src sv{};  // V source of the next iteration's loads
+  auto prologue = [&]() __attribute__((always_inline)) {
+    sv = tile_src(2);
+    const Src t0 = tile_src(0), t1 = tile_src(1);
+    issue(t0, 0, t0, 0);
+    issue(t1, 1, t0, 0);
+    issue(sv, 2, t1, 1);
+    uint4* vz = reinterpret_cast<uint4*>(smem + kVOff + 3 * kTileBytes);
+#pragma unroll
+    for (int j = 0; j < kTileBytes / 16 / kTL; ++j) vz[tid + kTL * j] = make_uint4(0, 0, 0, 0);
+  };
+  const bool early = n_prefix_tiles >= 3;
+  if (early) prologue();
+
   // ---- which 64-node tree tiles any row of this workgroup can see
   if (tid == 0) *s_tree_mask = 0;
   __syncthreads();
@@ -213,93 +318,11 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     if (m) atomicOr(s_tree_mask, m);
   }
   __syncthreads();
-  const uint32_t tree_mask = do_tree ? *s_tree_mask : 0u;
-  const int n_tiles = n_prefix_tiles + __popc(tree_mask);
-
-  f32x16_t acc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) acc[d] = f32x16_t{};
-  float m_out = -INFINITY, l = 0.0f;
+  tree_mask = do_tree ? *s_tree_mask : 0u;
+  n_tiles = n_prefix_tiles + __popc(tree_mask);
 
   if (n_tiles > 0) {
-    const char* kc = static_cast<const char*>(a.k_cache);
-    const char* vc = static_cast<const char*>(a.v_cache);
-    const char* kt = static_cast<const char*>(a.k_tree);
-    const char* vt = static_cast<const char*>(a.v_tree);
-    auto tile_kind = [&](int it, int& kind, int& base) __attribute__((always_inline)) {
-      if (it < n_prefix_tiles) {
-        kind = 0;
-        base = (kb0 + it) * kKT;
-      } else {
-        uint32_t m = tree_mask;
-        for (int j = it - n_prefix_tiles; j > 0; --j) m &= m - 1;
-        kind = 1;
-        base = __ffs(m) - 1;
-      }
-    };
-    const __attribute__((address_space(4))) int32_t* bt_row =
-        (const __attribute__((address_space(4))) int32_t*)(a.block_table) +
-        static_cast<long>(b) * a.max_blocks;
-    // staging lanes: load j (0, 1) of wave w covers tile rows 32 j + 4 w .. +3, lane l
-    // the row 32 j + 4 w + l / 16 and LDS chunk l % 16; the ancestor load takes the
-    // low word of row 32 w + l in lanes 0-31 and the high word in lanes 32-63
-    const int lrow = 4 * wave + (lane >> 4);
-    const int kcb = (((lane & 15) ^ (lrow & 15)) << 4);        // K: chunk c at c ^ (key & 15)
-    const int vcb = (((lane & 15) ^ ((lrow & 3) << 2)) << 4);  // V: chunk c at c ^ ((key & 3) << 2)
-    const char* anc_base = reinterpret_cast<const char*>(a.anc + static_cast<long>(n0) * a.words);
-    const uint32_t anc_lane =
-        static_cast<uint32_t>(min((r0 + rl) / a.group, count - 1) * a.words * 8 + 4 * half);
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lds_kv = lds_addr(smem) + wave_u * 1024;
-    const uint32_t lds_anc = lds_addr(smem) + kAncOffL + wave_u * 256;
-
-    // source of tile it (clamped to the last tile)
-    struct Src {
-      const char* k;
-      const char* v;
-      uint32_t o0, o1;  // byte offsets of this lane's two rows (before the chunk offset)
-      uint32_t anc;     // this lane's byte offset of the tile's ancestor dword
-    };
-    auto tile_src = [&](int it) __attribute__((always_inline)) -> Src {
-      int kind, base;
-      tile_kind(min(it, n_tiles - 1), kind, base);
-      Src s;
-      int stride, nvalid;
-      if (kind == 0) {
-        s.anc = anc_lane;
-        stride = kD * 2;
-        const int blk = bt_row[base / kKT];
-        nvalid = min(kKT, plen - base);
-        if (blk < 0 || blk >= a.num_blocks) {
-          if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
-          s.k = kc;  // block 0 stands in; the sequence is flagged
-          s.v = vc;
-          nvalid = 1;
-        } else {
-          const long off = (static_cast<long>(blk) * a.hkv + g) * kKT * kD * 2;
-          s.k = kc + off;
-          s.v = vc + off;
-        }
-      } else {
-        s.anc = anc_lane + base * 8;
-        stride = a.hkv * kD * 2;
-        const long off = (static_cast<long>(n0 + base * 64) * a.hkv + g) * kD * 2;
-        s.k = kt + off;
-        s.v = vt + off;
-        nvalid = min(64, count - base * 64);
-      }
-      s.o0 = min(lrow, nvalid - 1) * stride;
-      s.o1 = min(32 + lrow, nvalid - 1) * stride;
-      return s;
-    };
-    // the loads of one iteration: K and ancestor words of the tile of sk, V of sv
-    auto issue = [&](const Src& sk, int slot_k, const Src& sv, int slot_v)
-        __attribute__((always_inline)) {
-      issue_loads(sk.k, sk.o0 + kcb, sk.o1 + kcb, lds_kv + slot_k * kTileBytes, anc_base, sk.anc,
-                  lds_anc + slot_k * kAncSlotBytes, sv.v, sv.o0 + vcb, sv.o1 + vcb,
-                  lds_kv + kVOff + slot_v * kTileBytes);
-    };
-
+    if (!early) prologue();
     const float c2 = a.scale * kLog2e;
     // per-lane LDS bases of the MFMA operands; slot, half and step are instruction offsets
     const int krow0 = key_perm(col);
@@ -444,7 +467,6 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     for (int v = 0; v < 8; ++v) px[v] = 0u;
 
     // tile iteration i (ring slot S = i % 4) = half-steps 2i and 2i+1
-    Src sv = tile_src(2);  // V source of the next iteration's loads
     auto body = [&](int i, auto slot) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
       const Src sk = tile_src(i + 3);
@@ -461,18 +483,8 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       wait_loads_and_barrier<kLoadsPerIter>();
     };
 
-    // prologue: three groups of loads in the iteration pattern, K(0), K(1) and K(2)
-    // with their ancestor words and V(0), V(0), V(1); V slot 3, read as "tile -1" by
-    // the first half-step with zero probabilities, is cleared
-    {
-      const Src t0 = tile_src(0), t1 = tile_src(1);
-      issue(t0, 0, t0, 0);
-      issue(t1, 1, t0, 0);
-      issue(sv, 2, t1, 1);
-      uint4* vz = reinterpret_cast<uint4*>(smem + kVOff + 3 * kTileBytes);
-#pragma unroll
-      for (int j = 0; j < kTileBytes / 16 / kTL; ++j) vz[tid + kTL * j] = make_uint4(0, 0, 0, 0);
-    }
+    // prologue (issued above): three groups of loads in the iteration pattern, K(0),
+    // K(1) and K(2) with their ancestor words and V(0), V(0), V(1)
     wait_loads_and_barrier<kLoadsPerIter>();
     if (wave_live) {  // scores of tile 0 half 0
 #pragma unroll
