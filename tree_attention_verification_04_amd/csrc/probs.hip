@@ -25,6 +25,7 @@ constexpr int kRowThreads = 256;
 constexpr int kRowChunk = 8192;                      // elements per workgroup
 constexpr int kPerThread = kRowChunk / kRowThreads;  // 32
 constexpr int kRowGroup = 8;                         // most output rows per write workgroup
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct RowArgs {
   const float* logits;
@@ -148,9 +149,10 @@ __global__ void __launch_bounds__(kRowThreads) k_row_write(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < kPerThread / 4; ++j) {
         const int k = k0 + 4 * (threadIdx.x + kRowThreads * j);
-        if (k < k1)
-          *reinterpret_cast<float4*>(a.probs + out + k) =
-              make_float4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+        if (k < k1) {  // streaming store: the rows are written once and not read here
+          const f32x4_t v = {p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(a.probs + out + k));
+        }
       }
     } else {
 #pragma unroll
