@@ -102,6 +102,16 @@ def test_attention_host_checks(lib):
     assert lse_off % 256 == 0 and (lse_off + rows * 4) % 256 == 0
     assert lib.tree_verify_attention_workspace_size(8, 4672, 584, 4096, 32, 8, 128,
                                                     tv.TV_DTYPE_BF16) == lse_off + rows * 4 + 64 * 4
+    # one die's worth of items past full rounds decides the cut: 8 pairs x 41 row tiles
+    # leave 9 items per die in the last round, cut in 3 pieces (3 rounds of a third of an
+    # item, ceil(27/32) = 1, beat 2 pieces: ceil(18/32) / 2 + 0.02); 8 pairs x 33 row
+    # tiles leave 1, cut in 7
+    for max_nodes, plen, tail, pieces in ((1312, 512, 9, 3), (1025, 100, 1, 7)):
+        rows = 8 * tail * pieces * 256
+        lse_off = counters + rows * 128 * 4
+        order_off = (lse_off + rows * 4 + 255) // 256 * 256
+        assert lib.tree_verify_attention_workspace_size(1, max_nodes, max_nodes, plen, 64, 8, 128,
+                                                        tv.TV_DTYPE_BF16) == order_off + 8 * 4
     # a single short verify: 32 pairs x 5 prefix splits of 64 rows
     rows = 5 * 64 * 32
     assert need == counters + rows * 128 * 4 + rows * 4

@@ -199,6 +199,40 @@ def test_attention_workspace_counters_left_zero(gpu_lib, name):
     assert np.abs(to_f64(outs[0][0])[rows] - want[rows]).max() <= TOL_BF16
 
 
+def test_attention_workspace_shared_across_plans(gpu_lib):
+    """One zero-filled workspace serves calls of different launch plans in turn
+    (persistent with cut items, prefix splits, persistent, one plain round): each
+    output equals the output with a workspace of its own, bit for bit."""
+    names = ["persistent_tail", "splits16", "persistent", "one_round"]
+    # one_round: 32 pairs x 8 row tiles = 32 items per die, no split: a plain launch
+    specs = dict(COUNTER_CASES,
+                 one_round=([W.tree_random(np.random.default_rng(50), 512, 8)] * 4,
+                            [300, 200, 100, 64], 32, 8))
+    runs = []
+    for name in names:
+        parents, plens, hq, hkv = specs[name]
+        case = W.make_case(name, parents, plens, hq, hkv, 128, W.DT_BF16, 10, 29, with_probs=False)
+        dev = W.case_to_device(case, probs=False)
+        anc, _, _, _ = gpu_index(gpu_lib, case, dev)
+        runs.append((case, dev, anc))
+    sizes = [gpu_lib.tree_verify_attention_workspace_size(c.batch, c.total_nodes, max(1, c.max_nodes),
+                                                          c.max_prefix, c.hq, c.hkv, 128,
+                                                          gpu_lib.TV_DTYPE_BF16) for c, _, _ in runs]
+    shared = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        for (case, dev, anc), need in zip(runs, sizes):
+            args = (dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"], dev["prefix_len"],
+                    dev["k_tree"], dev["v_tree"], dev["cu_nodes"], anc, max(1, case.max_nodes),
+                    case.max_prefix)
+            out, lse, err = gpu_lib.tree_verify_attention(*args, workspace=shared)
+            own, own_lse, _ = gpu_lib.tree_verify_attention(
+                *args, workspace=torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda"))
+            torch.cuda.synchronize()
+            assert int(err.item()) == 0
+            assert torch.equal(out, own) and torch.equal(lse, own_lse), case.name
+            assert int(shared[:2048].count_nonzero().item()) == 0
+
+
 def test_attention_aliased_block_tables(gpu_lib):
     parents = [W.tree_kary_levels(3, 3)] * 4
     case = W.make_case("alias", parents, [700] * 4, 8, 2, 128, W.DT_BF16, 10, 3, alias_prefix=True,
