@@ -93,7 +93,7 @@ __device__ __forceinline__ uint16_t pack_info(int ctx, int slot) {
 // importance weights and renormalised probabilities, then per row / node scalars
 constexpr int kRowSlots = (kMaxDraftNodes + 1) * kMaxDraftK;
 constexpr int kOffW = 0;
-constexpr int kOffWRow = kOffW + kMaxCand * 8;
+constexpr int kOffWRow = kOffW + kMaxCand * 8;  // reads up to 3 entries past s_w land here
 constexpr int kOffQ = kOffWRow + kRowSlots * 8;
 constexpr int kOffInfo = kOffQ + kRowSlots * 4;
 constexpr int kOffU = kOffInfo + kMaxCand * 2;
@@ -197,8 +197,17 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
     // chunk sums, then a scan of them across the wavefront
     const int chunk = (n_cand + 63) / 64;
     const int c0 = min(n_cand, lane * chunk), c1 = min(n_cand, c0 + chunk);
+    // weights read 4 at a time (the LDS latency once per 4), added in candidate order;
+    // entries past the chunk are read (inside the LDS block: s_wrow follows s_w) but
+    // count as +0.0, which leaves a sum of non-negative weights unchanged
     double ls = 0.0;
-    for (int j = c0; j < c1; ++j) ls += s_w[j];
+    for (int j = c0; j < c1; j += 4) {
+      double v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = s_w[j + e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ls += j + e < c1 ? v[e] : 0.0;
+    }
     const double incl = wave_incl_scan(ls);
     const double excl = dpp_shift(incl, 0x138, 0xf);  // wave_shr:1; lane 0 gets 0
     const double total = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(incl), 63),
@@ -211,12 +220,16 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
     if (lane == owner) {
       double run = excl;
       int last = -1;
-      for (int j = c0; j < c1; ++j) {
-        if (s_w[j] > 0.0) last = j;
-        run += s_w[j];
-        if (run > t) {
-          pick = j;
-          break;
+      for (int j = c0; j < c1 && pick < 0; j += 4) {  // 4 weights per LDS round trip
+        double v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = s_w[j + e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (pick >= 0 || j + e >= c1) continue;
+          if (v[e] > 0.0) last = j + e;
+          run += v[e];
+          if (run > t) pick = j + e;
         }
       }
       if (pick < 0) pick = last;  // rounding left the chunk's walk short: its last live entry
