@@ -331,12 +331,18 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
   __shared__ uint64_t s_rem;
   __shared__ uint64_t s_part[2 * kMaxResidChunks];
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int c = ws_c[b];
-  if (c < 0) return;
-  const int n0 = cu_nodes[b];
+  // the rejection node, the sequence's first node and the per-chunk sums (which do
+  // not depend on the node) are requested together; then the node's uniform
   const uint64_t* mine = part + static_cast<long>(b) * chunks * 2;
-  // the per-chunk sums, loaded by all threads at once, then scanned from LDS
-  for (int k = tid; k < 2 * chunks; k += kAcceptThreads) s_part[k] = mine[k];
+  const int c = ws_c[b];
+  const int n0 = cu_nodes[b];
+  uint64_t pv[2 * kMaxResidChunks / kAcceptThreads + 1];
+  int np = 0;
+  for (int k = tid; k < 2 * chunks; k += kAcceptThreads) pv[np++] = mine[k];
+  if (c < 0) return;
+  const float u = u_res[n0 + c];
+  np = 0;
+  for (int k = tid; k < 2 * chunks; k += kAcceptThreads) s_part[k] = pv[np++];
   __syncthreads();
   if (tid == 0) {
     uint64_t zr = 0, zt = 0;
@@ -347,7 +353,7 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
     const int mode = zr > 0 ? 0 : (zt > 0 ? 1 : -1);
     s_mode = mode;
     if (mode >= 0) {
-      const uint64_t t = exact_threshold(u_res[n0 + c], mode == 0 ? zr : zt);
+      const uint64_t t = exact_threshold(u, mode == 0 ? zr : zt);
       uint64_t cum = 0;
       int kc = chunks - 1;
       for (int k = 0; k < chunks; ++k) {
@@ -371,21 +377,30 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
   const long row = static_cast<long>(n0 + c) * vocab;
   const int k0 = s_chunk * kResidChunk + tid * kResidPerThread;
   const int k1 = min(vocab, min(k0 + kResidPerThread, (s_chunk + 1) * kResidChunk));
+  // this thread's weights, loaded once (all loads in flight together) and kept for
+  // the walk
+  uint64_t wgt[kResidPerThread];
+#pragma unroll
+  for (int e = 0; e < kResidPerThread; ++e) {
+    const int k = k0 + e;
+    wgt[e] = 0;
+    if (k < k1) wgt[e] = mode == 0 ? resid_weight(pt[row + k], pd[row + k]) : target_weight(pt[row + k]);
+  }
   uint64_t local = 0;
-  for (int k = k0; k < k1; ++k)
-    local += mode == 0 ? resid_weight(pt[row + k], pd[row + k]) : target_weight(pt[row + k]);
+#pragma unroll
+  for (int e = 0; e < kResidPerThread; ++e) local += wgt[e];
   uint64_t total;
   const uint64_t excl = block_exclusive_scan(local, &total);
   const uint64_t rem = s_rem;
   if (local > 0 && excl <= rem && rem < excl + local) {
     uint64_t run = excl;
-    for (int k = k0; k < k1; ++k) {
-      run += mode == 0 ? resid_weight(pt[row + k], pd[row + k]) : target_weight(pt[row + k]);
-      if (run > rem) {
-        resample_token[b] = k;
-        break;
-      }
+    int tok = -1;
+#pragma unroll
+    for (int e = 0; e < kResidPerThread; ++e) {
+      run += wgt[e];
+      if (tok < 0 && run > rem) tok = k0 + e;
     }
+    resample_token[b] = tok;
   }
 }
 
