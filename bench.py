@@ -514,6 +514,10 @@ def main():
     roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
                 alg_bytes=int(bytes_), alg_flops=float(flops))
 
+    # the step's outcome (the same every step: fixed inputs): tokens it accepts, the
+    # accepted paths plus the resampled tokens, as context beside the verified rate
+    torch.cuda.synchronize()
+    accepted = int(acc_out["accept_len"].sum().item()) + int((acc_out["resample_token"] >= 0).sum().item())
     commit = measure_commit(tv, case, dev, acc_out, max_path, reps)
     softmax = measure_softmax(tv, case, reps)
     fp8 = measure_fp8(tv, case, dev, anc, mn, attn_us, reps)
@@ -540,6 +544,10 @@ def main():
                    "timing": "HIP-graph replay, events on the launch stream",
                    "wall_s": round(wall, 3)},
         "roofline": roof,
+        "accepted": {"tokens_per_step": accepted,
+                     "tokens_per_s": round(accepted / (ms_step * 1e-3), 1),
+                     "note": "accepted path lengths + resampled tokens; the synthetic target "
+                             "and draft rows are independent draws, not a model's"},
         "next_rows": {"kv_commit": commit, "softmax_rows": softmax, "fp8_kv_attention": fp8,
                       "draft_tree": draft},
     }
