@@ -79,6 +79,8 @@ SMALL = {
     "no_prefix": ([W.tree_star(100)], [0], 4, 2),
     "ragged_batch": ([W.tree_random(np.random.default_rng(10), 60, 5), W.tree_chain(5),
                       W.tree_random(np.random.default_rng(11), 300, 12)], [1000, 37, 513], 4, 4),
+    # 512 (sequence, KV head) pairs: 64 work items per die, run by the persistent launch
+    "many_pairs": ([W.tree_heap(5)] * 64, [64 + 7 * b for b in range(64)], 32, 8),
 }
 
 
@@ -90,9 +92,10 @@ def test_fp8_attention_small(gpu_lib, name, mode):
     check_fp8(gpu_lib, case, mode, seed=31)
 
 
-@pytest.mark.parametrize("index", [1, 3])
+@pytest.mark.parametrize("index", [1, 2, 3])
 def test_fp8_attention_full_configs(gpu_lib, index):
-    """The LLaVA-like and the serving workloads with quantized caches, sampled nodes."""
+    """The LLaVA-like, wide-tree and serving workloads with quantized caches, sampled
+    nodes."""
     case = W.make_config(index, with_probs=False)
     seqs = None if case.batch <= 8 else {0, 7, 31, 63}
     check_fp8(gpu_lib, case, "quant", seed=index,
