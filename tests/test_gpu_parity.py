@@ -233,6 +233,30 @@ def test_attention_workspace_shared_across_plans(gpu_lib):
             assert int(shared[:2048].count_nonzero().item()) == 0
 
 
+def test_attention_persistent_bad_block_and_prefix(gpu_lib):
+    """A persistent launch (512 pairs) with one sequence's block id out of range and
+    another's prefix longer than max_prefix: the block error bit is set, nothing
+    faults, and every other sequence's output still matches the oracle."""
+    parents = [W.tree_random(np.random.default_rng(60 + b), 40 + b % 50, 8) for b in range(64)]
+    plens = [300 + 41 * b for b in range(64)]
+    case = W.make_case("badpers", parents, plens, 32, 8, 128, W.DT_BF16, 10, 37, with_probs=False)
+    dev = W.case_to_device(case, probs=False)
+    mn = max(1, case.max_nodes)
+    anc, _, _, _ = gpu_index(gpu_lib, case, dev)
+    dev["block_table"][5, 1] = case.k_cache.shape[0] + 7   # sequence 5: a block id past the pool
+    dev["prefix_len"][9] = case.max_prefix + 1             # sequence 9: longer than max_prefix
+    out, lse, err = gpu_lib.tree_verify_attention(
+        dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"], dev["prefix_len"],
+        dev["k_tree"], dev["v_tree"], dev["cu_nodes"], anc, mn, case.max_prefix)
+    torch.cuda.synchronize()
+    assert int(err.item()) & oracle.ERR_BLOCK
+    nodes = sample_nodes(case, 4, seed=6, seqs={0, 4, 6, 8, 10, 63})
+    want, _ = oracle_attention(case, nodes)
+    rows = rows_of(case, nodes)
+    assert np.isfinite(to_f64(out)[rows]).all()
+    assert np.abs(to_f64(out)[rows] - want[rows]).max() <= TOL_BF16
+
+
 def test_attention_aliased_block_tables(gpu_lib):
     parents = [W.tree_kary_levels(3, 3)] * 4
     case = W.make_case("alias", parents, [700] * 4, 8, 2, 128, W.DT_BF16, 10, 3, alias_prefix=True,
