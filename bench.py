@@ -86,6 +86,25 @@ def recorded_traffic(config: int):
     return int(kv["hbm_bytes_per_launch"])
 
 
+def measured_copy_gbps(torch) -> float:
+    """Device-to-device copy rate (bytes read + written per second) of 1 GiB, the
+    best of 5 copies timed with events: the attainable HBM rate beside the published
+    peak (context for the roofline fraction, which stays against the peak)."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    return round(2 * n * 4 / (best * 1e-3) / 1e9, 1)
+
+
 def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> None:
     """Turn FETCH_SIZE / WRITE_SIZE passes into bytes per attention launch.
 
@@ -512,7 +531,8 @@ def main():
                     frac=round(ach / cpeak, 4), traffic=None)
     roof["traffic"] = recorded_traffic(args.config)
     roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
-                alg_bytes=int(bytes_), alg_flops=float(flops))
+                alg_bytes=int(bytes_), alg_flops=float(flops),
+                measured_copy_GBps=measured_copy_gbps(torch))
 
     # the step's outcome (the same every step: fixed inputs): tokens it accepts, the
     # accepted paths plus the resampled tokens, as context beside the verified rate
