@@ -510,8 +510,9 @@ __global__ void __launch_bounds__(kThreads) k_attn_mfma(AttnArgs a) {
 // Merge of the prefix splits, one thread per (row, 4 consecutive d):
 //   lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * out_s
 // All splits' values are loaded before any is used (one memory round trip); kS is
-// the split count rounded up to a power of two, the loads past the last split
-// re-read it and get weight zero.
+// the split count rounded up to an instance (2, 4, 5, 8 or 16; 5 is a short verify
+// with a 17-block prefix), the loads past the last split re-read it and get weight
+// zero.
 template <int kS>
 __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
   int zero;
@@ -588,6 +589,8 @@ int launch_attn_combine(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_attn_combine<2>, grid, block, 0, s, a);
   else if (a.splits <= 4)
     hipLaunchKernelGGL(k_attn_combine<4>, grid, block, 0, s, a);
+  else if (a.splits <= 5)  // a single short verify (17-block prefix: 5 splits of 4)
+    hipLaunchKernelGGL(k_attn_combine<5>, grid, block, 0, s, a);
   else if (a.splits <= 8)
     hipLaunchKernelGGL(k_attn_combine<8>, grid, block, 0, s, a);
   else
