@@ -22,8 +22,15 @@ Readings taken where the pages are silent (each also listed in the design notes)
     longest path ends at the accepted node of largest depth; ties go to the
     smallest node index.  Nothing accepted -> length 0.
   * The rejection point is the smallest-index child of the path's last node
-    (or the smallest-index node under the prefix if nothing was accepted).  A
-    fully accepted leaf has no rejection point: nothing is resampled (-1).
+    (or the smallest-index node under the prefix if nothing was accepted).
+  * Bonus token at a fully accepted leaf: the target's single forward pass over
+    the tree gives a distribution at every node's own context (page [P537]
+    §2.2.3: one forward pass yields logits at every node), so when the path's
+    last node w has no child, the caller may pass p_target at w's own context
+    (own_row[w], a row of p_own) and the extra token is drawn from it with
+    u_resample[w]: the step then always emits accepted + 1 tokens, as plain
+    speculative sampling does (page [P525] §1.2).  Without that row nothing is
+    resampled (-1).  An own_row entry outside [-1, own_rows) sets ERR_ROW.
   * Sampling is an integer inverse CDF: weights q_k = floor(r_k * 2^40) with
     r_k = (double)pt_k - (double)pd_k (0 where r_k <= 0), Z = sum q_k, the
     uniform u = M * 2^E taken exactly, T = floor(M * Z * 2^E), token = the
@@ -36,6 +43,7 @@ import math
 
 import numpy as np
 
+from .probs import ERR_ROW
 from .tree import (ERR_BAD_PARENT, ERR_PATH, ERR_TOKEN, ERR_UNIFORM, ERR_ZERO_MASS,
                    ancestors_or_self, parent_errors)
 
@@ -93,6 +101,18 @@ def residual_token(row_t: np.ndarray, row_d: np.ndarray, u: float):
     return k, 0
 
 
+def target_token(row_t: np.ndarray, u: float):
+    """Token drawn from norm(p_target row) with uniform u (the bonus token), by the
+    same integer inverse CDF.  Returns (token, err_bits); -1 when the row has no mass."""
+    q = fixed_weights(row_t, None)
+    z = int(q.sum(dtype=np.uint64))
+    if z == 0:
+        return -1, ERR_ZERO_MASS
+    t = threshold(u, z)
+    csum = np.cumsum(q, dtype=np.uint64)
+    return int(np.searchsorted(csum, np.uint64(t), side="right")), 0
+
+
 def _dfs_accepted(parent: np.ndarray, acc: list[bool]) -> list[bool]:
     """Walk from the prefix down, entering a node only if it passed its test.
 
@@ -114,10 +134,13 @@ def _dfs_accepted(parent: np.ndarray, acc: list[bool]) -> list[bool]:
 
 
 def accept_sequence(pt: np.ndarray, pd: np.ndarray, token: np.ndarray, u_acc: np.ndarray,
-                    u_res: np.ndarray, parent: np.ndarray, vocab: int, max_path: int):
+                    u_res: np.ndarray, parent: np.ndarray, vocab: int, max_path: int,
+                    p_own=None, own_row=None):
     """Acceptance for one sequence; all arrays are that sequence's local slices.
 
-    pt / pd may be any row-indexable [N, vocab] arrays.
+    pt / pd may be any row-indexable [N, vocab] arrays.  p_own [R, vocab] and
+    own_row [N] (row of p_own at each node's own context, -1 = none) are optional:
+    with them a fully accepted leaf draws the bonus token.
     Returns dict(accept_len, path (list, -1 padded to max_path), resample_node,
     resample_token, node_ok (list of 0/1), err).
     """
@@ -156,16 +179,32 @@ def accept_sequence(pt: np.ndarray, pd: np.ndarray, token: np.ndarray, u_acc: np
         else:
             rtok, e = residual_token(np.asarray(pt[c]), np.asarray(pd[c]), float(u_res[c]))
             err |= e
+    elif w >= 0 and own_row is not None:
+        # the path ends at a leaf: bonus token from p_target at w's own context
+        r = int(own_row[w])
+        if r < -1 or (p_own is not None and r >= len(p_own)) or (p_own is None and r >= 0):
+            err |= ERR_ROW
+        elif r >= 0:
+            c = w
+            if not uniform_ok(u_res[w]):
+                err |= ERR_UNIFORM
+            else:
+                rtok, e = target_token(np.asarray(p_own[r]), float(u_res[w]))
+                err |= e
     return dict(accept_len=accept_len, path=path, resample_node=c, resample_token=rtok,
                 node_ok=[1 if o else 0 for o in ok], err=err)
 
 
 def accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, vocab: int,
-           max_path: int):
+           max_path: int, p_own=None, own_row=None):
     """Acceptance for a batch of flattened trees.
 
+    p_own [R, vocab] / own_row [total] (global node indexing, -1 = none): optional
+    own-context target rows for bonus tokens at fully accepted leaves.
     Returns dict of numpy arrays: accept_len [B], path [B, max_path],
     resample_node [B], resample_token [B], node_ok [total] uint8, err (int).
+    resample_node is the rejection node c whose residual was sampled, or, for a
+    bonus token, the path's last node w itself.
     """
     bsz = len(cu_nodes) - 1
     total = int(cu_nodes[-1])
@@ -175,7 +214,8 @@ def accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, voc
     for b in range(bsz):
         n0, n1 = int(cu_nodes[b]), int(cu_nodes[b + 1])
         r = accept_sequence(p_target[n0:n1], p_draft[n0:n1], token[n0:n1], u_accept[n0:n1],
-                            u_resample[n0:n1], parent[n0:n1], vocab, max_path)
+                            u_resample[n0:n1], parent[n0:n1], vocab, max_path, p_own,
+                            None if own_row is None else own_row[n0:n1])
         out["accept_len"][b] = r["accept_len"]
         out["path"][b] = r["path"]
         out["resample_node"][b] = r["resample_node"]
