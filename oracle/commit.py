@@ -18,7 +18,13 @@ Readings taken where the pages are silent:
     prefix length grows by the accepted length;
   * a sequence whose path is invalid (accepted length outside [0, max_path], a
     path entry outside its nodes) or whose new positions are not mapped to a
-    valid block gets the error bit and is left untouched.
+    valid block gets the error bit and is left untouched;
+  * a block the new positions fall in must be the sequence's own: prefix blocks
+    may be shared by several sequences for reading (page [P537] §2.3.3, shared
+    prefix pool), but when another sequence's table row also maps a destination
+    block (anywhere in that row), writing it would change that sequence's
+    prefix, so the commit sets the block error bit and leaves the sequence
+    untouched (copying a shared block before writing is the caller's job).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 """
@@ -59,6 +65,10 @@ def commit_kv(k_cache, v_cache, block_table, prefix_len, num_blocks: int, k_tree
             continue
         blocks = [int(block_table[b, t // BLOCK]) for t in positions]
         if any(blk < 0 or blk >= num_blocks for blk in blocks):
+            err |= ERR_BLOCK
+            continue
+        others = {int(x) for o in range(len(cu_nodes) - 1) if o != b for x in block_table[o]}
+        if any(blk in others for blk in blocks):
             err |= ERR_BLOCK
             continue
         for j, t in enumerate(positions):

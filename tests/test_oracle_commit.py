@@ -124,3 +124,47 @@ def test_planted_off_by_one_is_caught():
     want = np.concatenate([gather_prefix(case.k_cache, case.block_table[0], 62),
                            case.k_tree[path[0, :5]]], axis=0)
     assert not np.array_equal(gather_prefix(kc, case.block_table[0], 67), want)
+
+
+def shared_prefix_tables(case, shared_blocks: int):
+    """Sequence 1's first `shared_blocks` logical blocks mapped to sequence 0's blocks."""
+    bt = case.block_table.copy()
+    bt[1, :shared_blocks] = bt[0, :shared_blocks]
+    return bt
+
+
+def test_commit_into_a_shared_block_is_refused():
+    """Two sequences share a 100-token prefix (its second block is partly filled):
+    both would append into that block, so neither is written and the block bit is
+    set; a third, private sequence is committed."""
+    case = chain_case([100, 100, 40], [3, 3, 3])
+    bt = shared_prefix_tables(case, 2)
+    acc, path = paths_of(case, [3, 3, 3], 4)
+    kc, vc, pl, err = oracle.commit_kv(case.k_cache, case.v_cache, bt, case.prefix_len,
+                                       case.num_blocks, case.k_tree, case.v_tree, case.cu_nodes,
+                                       acc, path, 4)
+    assert err == oracle.ERR_BLOCK
+    assert list(pl) == [100, 100, 43]
+    changed = {int(x) for x in np.argwhere(np.any(kc != case.k_cache, axis=(1, 2, 3)))[:, 0]}
+    assert changed == {int(bt[2, 0])}
+    # the shared prefix reads back unchanged through both tables
+    for b in (0, 1):
+        np.testing.assert_array_equal(gather_prefix(kc, bt[b], 100),
+                                      gather_prefix(case.k_cache, bt[0], 100))
+
+
+def test_commit_after_a_shared_whole_block_prefix():
+    """A shared prefix of whole blocks (128 tokens) is only read: each sequence
+    appends into a private block, no error, and the gather pin holds for both."""
+    case = chain_case([128, 128], [4, 2])
+    bt = shared_prefix_tables(case, 2)
+    acc, path = paths_of(case, [4, 2], 4)
+    kc, vc, pl, err = oracle.commit_kv(case.k_cache, case.v_cache, bt, case.prefix_len,
+                                       case.num_blocks, case.k_tree, case.v_tree, case.cu_nodes,
+                                       acc, path, 4)
+    assert err == 0 and list(pl) == [132, 130]
+    for b, n in enumerate([4, 2]):
+        n0 = int(case.cu_nodes[b])
+        want = np.concatenate([gather_prefix(case.k_cache, bt[b], 128),
+                               case.k_tree[n0 + path[b, :n]]], axis=0)
+        np.testing.assert_array_equal(gather_prefix(kc, bt[b], 128 + n), want)
