@@ -274,7 +274,12 @@ int tree_accept(const float* p_target, const float* p_draft, const int32_t* toke
  * the accepted path; [P525] §2.3.2, the tree's KV slots return to the pool after
  * verification; [P525] §8.1, accepted length and new KV indices as verify outputs).
  * The block table must already map the logical blocks of the new positions (the
- * caller reserves them; nothing is allocated here).
+ * caller reserves them; nothing is allocated here), and those blocks must belong
+ * to this sequence alone: prefix blocks may be shared between sequences for
+ * reading ([P537] §2.3.3, shared prefix pool), but a block that another
+ * sequence's table row also maps is not written (a shared prefix whose length is
+ * not a multiple of 64 ends inside such a block; copying it first is the
+ * caller's job).
  *
  *   k_tree/v_tree   [total_nodes, hkv, head_dim], dtype (must not overlap the cache)
  *   cu_nodes        [batch + 1] int32
@@ -283,9 +288,11 @@ int tree_accept(const float* p_target, const float* p_draft, const int32_t* toke
  *   block_table     [batch, max_blocks] int32
  *   prefix_len      [batch] int32: read, then increased in place
  *   head_dim 64 or 128; dtype TV_DTYPE_F32 or TV_DTYPE_BF16
+ *   max_path        at most 4096 (else TV_EUNSUPPORTED)
  *   err             TV_ERR_PATH (accept_len outside [0, max_path], or a path entry
  *                   outside the sequence's nodes), TV_ERR_BLOCK (a new position beyond
- *                   the table or mapped to a block outside [0, num_blocks)); such a
+ *                   the table, mapped to a block outside [0, num_blocks), or mapped to a
+ *                   block that another sequence's table row also holds); such a
  *                   sequence is left untouched (cache and prefix_len)
  */
 int tree_commit_kv(const void* k_tree, const void* v_tree, const int32_t* cu_nodes,

@@ -109,3 +109,24 @@ def test_commit_errors(gpu_lib):
                             max_path)
     assert want[3] == oracle.ERR_BLOCK | oracle.ERR_PATH
     assert_commit_equal(got, want)
+
+
+@pytest.mark.parametrize("plen, shared", [(100, 2), (128, 2)])
+def test_commit_shared_prefix_blocks(gpu_lib, plen, shared):
+    """Sequences 0 and 1 share their first blocks.  A 100-token shared prefix ends
+    inside a shared block: neither sequence may append there (block bit, both left
+    untouched, the private third one committed).  A 128-token one ends on a block
+    boundary: every sequence appends into a private block."""
+    case = chain_case([plen, plen, 40], [3, 3, 3], 8, 2, 128, W.DT_BF16, seed=13)
+    case.block_table = case.block_table.copy()
+    case.block_table[1, :shared] = case.block_table[0, :shared]
+    max_path = 4
+    acc = np.array([3, 3, 3], dtype=np.int32)
+    path = np.tile(np.arange(max_path, dtype=np.int32), (case.batch, 1))
+    dev = W.case_to_device(case, probs=False)
+    got = run_commit(gpu_lib, case, dev, acc, path)
+    want = oracle.commit_kv(case.k_cache, case.v_cache, case.block_table, case.prefix_len,
+                            case.num_blocks, case.k_tree, case.v_tree, case.cu_nodes, acc, path,
+                            max_path)
+    assert want[3] == (oracle.ERR_BLOCK if plen % 64 else 0)
+    assert_commit_equal(got, want)

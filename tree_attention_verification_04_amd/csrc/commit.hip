@@ -9,10 +9,14 @@
 // slots return to the pool after verification).
 //
 // One workgroup per sequence: thread 0 validates the path and the blocks the new
-// positions fall in, every thread copies 16-byte chunks of (path row, KV head), and
-// thread 0 writes the new prefix length after the copy (all threads read the old one
-// first).  Pure data movement: HBM-bound, 2 x rows x hkv x head_dim x elt bytes read
-// and written.
+// positions fall in, every thread then scans a stripe of the other sequences' table
+// rows for those blocks (a prefix block shared by several sequences may be read by
+// all of them, but the block a commit writes must be the sequence's own: a shared
+// prefix whose length is not a multiple of 64 ends inside such a block, and copying
+// on write is the caller's job), every thread copies 16-byte chunks of (path row, KV
+// head), and thread 0 writes the new prefix length after the copy (all threads read
+// the old one first).  Pure data movement: HBM-bound, 2 x rows x hkv x head_dim x
+// elt bytes read and written.
 #include "tv_common.h"
 
 namespace tv {
@@ -20,6 +24,8 @@ namespace tv {
 namespace {
 
 constexpr int kCommitThreads = 256;
+constexpr int kMaxPath = 4096;      // positions one commit may append
+constexpr int kMaxDestBlocks = kMaxPath / TV_BLOCK + 1;  // blocks they may fall in
 
 struct CommitArgs {
   const char* k_tree;
@@ -32,11 +38,12 @@ struct CommitArgs {
   const int32_t* block_table;
   int32_t* prefix_len;
   int32_t* err;
-  int max_path, hkv, row_bytes, num_blocks, max_blocks;
+  int max_path, hkv, row_bytes, num_blocks, max_blocks, batch;
 };
 
 __global__ void __launch_bounds__(kCommitThreads) k_commit_kv(CommitArgs a) {
-  __shared__ int s_ok;
+  __shared__ int s_ok, s_ndest;
+  __shared__ int s_dest[kMaxDestBlocks];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int n0 = a.cu_nodes[b];
@@ -55,17 +62,35 @@ __global__ void __launch_bounds__(kCommitThreads) k_commit_kv(CommitArgs a) {
       if (bits == 0 && len > 0) {
         if (p0 < 0 || static_cast<long>(p0) + len > static_cast<long>(a.max_blocks) * TV_BLOCK) {
           bits = TV_ERR_BLOCK;
+        } else if ((p0 + len - 1) / TV_BLOCK - p0 / TV_BLOCK >= kMaxDestBlocks) {
+          bits = TV_ERR_PATH;
         } else {
-          for (int lb = p0 / TV_BLOCK; lb <= (p0 + len - 1) / TV_BLOCK; ++lb)
+          for (int lb = p0 / TV_BLOCK; lb <= (p0 + len - 1) / TV_BLOCK; ++lb) {
             if (bt[lb] < 0 || bt[lb] >= a.num_blocks) bits = TV_ERR_BLOCK;
+            s_dest[lb - p0 / TV_BLOCK] = bt[lb];
+          }
         }
       }
     }
-    if (bits) atomicOr(a.err, bits);
-    s_ok = bits == 0;
+    s_ndest = bits == 0 && len > 0 ? (p0 + len - 1) / TV_BLOCK - p0 / TV_BLOCK + 1 : 0;
+    s_ok = bits;
   }
   __syncthreads();
-  if (!s_ok) return;
+  // a destination block that another sequence's table also maps is not written
+  const int ndest = s_ndest;
+  if (ndest > 0) {
+    bool shared = false;
+    const long entries = static_cast<long>(a.batch) * a.max_blocks;
+    for (long e = tid; e < entries; e += kCommitThreads) {
+      if (e / a.max_blocks == b) continue;
+      const int blk = a.block_table[e];
+      for (int d = 0; d < ndest; ++d) shared |= blk == s_dest[d];
+    }
+    if (shared) atomicOr(&s_ok, TV_ERR_BLOCK);
+    __syncthreads();
+  }
+  if (tid == 0 && s_ok) atomicOr(a.err, s_ok);
+  if (s_ok) return;
   const int chunks = a.row_bytes / 16;  // 16-byte chunks of one (row, KV head)
   const int items = len * a.hkv * chunks;
   for (int it = tid; it < items; it += kCommitThreads) {
@@ -104,6 +129,8 @@ extern "C" int tree_commit_kv(const void* k_tree, const void* v_tree, const int3
   if (dtype != TV_DTYPE_F32 && dtype != TV_DTYPE_BF16)
     return tv::fail(TV_EUNSUPPORTED, "tree_commit_kv: dtype must be F32 or BF16");
   if (err == nullptr) return tv::fail(TV_EINVAL, "tree_commit_kv: null err");
+  if (max_path > tv::kMaxPath)
+    return tv::fail(TV_EUNSUPPORTED, "tree_commit_kv: max_path must be at most 4096");
   if (batch == 0) return TV_OK;
   if (cu_nodes == nullptr || accept_len == nullptr || prefix_len == nullptr ||
       block_table == nullptr || k_cache == nullptr || v_cache == nullptr)
@@ -128,6 +155,7 @@ extern "C" int tree_commit_kv(const void* k_tree, const void* v_tree, const int3
   a.row_bytes = head_dim * (dtype == TV_DTYPE_F32 ? 4 : 2);
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
+  a.batch = batch;
   auto s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(tv::k_commit_kv, dim3(batch), dim3(tv::kCommitThreads), 0, s, a);
   return tv::check_launch("tree_commit_kv");
