@@ -6,18 +6,20 @@ layer) + tree_accept.  The step is captured once in a HIP graph and replayed
 (launch overhead is what graph capture removes from a verify step); the eager
 rate is reported beside it.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I] [--only]
 
---config selects the workload (0..4, default 1: LLaVA-7B-like single verify,
-batch 1, prefix 1088, 64-node importance-sampled tree, 32 heads MHA,
-head_dim 128, bf16, vocab 32000).
+--config selects the headline workload (0..4, default 4: long-context verify,
+batch 4, prefix 32768, 256-node trees, 64 query / 8 KV heads, head_dim 128,
+bf16, vocab 128256 -- the largest workload that fits one GPU).  The other four
+workloads are measured after it, each with its step time, attention time,
+roofline and CPU baseline, under "other_workloads" (--only skips them).
 
 `roofline` is for the attention call (the dominant kernel): algorithmic bytes
 (unique prefix K+V, tree K+V, Q, out) or flops (4*D*Hq*sum over nodes of the
 visible keys) per launch divided by its average duration, timed with events on
 the launch stream over back-to-back graph-replayed launches.  `cpu_baseline`
 is the CPU oracle (fp64 numpy + Python) timed on this host on a bounded
-number of whole steps of the same workload.
+sample of the same workload (whole steps, or the first sequences of one).
 """
 from __future__ import annotations
 
@@ -37,9 +39,16 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix
 VALU_FP32_PEAK_TFS = 157.3     # MI355X fp32 vector
 
 
+def node_depths(parent: np.ndarray) -> np.ndarray:
+    """Depth of each node of one tree (1 under the prefix); parents precede children."""
+    dep = np.zeros(len(parent), dtype=np.int64)
+    for i, p in enumerate(parent):
+        dep[i] = 1 if p < 0 else dep[p] + 1
+    return dep
+
+
 def attention_cost(case):
     """Algorithmic bytes and flops of one tree-attention launch."""
-    import oracle
     esz = 2 if case.dtype == 1 else 4
     d, hq, hkv = case.d, case.hq, case.hkv
     total = case.total_nodes
@@ -49,7 +58,7 @@ def attention_cost(case):
     bytes_ = (prefix_tokens * hkv * d * 2 + total * hkv * d * 2 + 2 * total * hq * d) * esz
     visible = 0
     for b in range(case.batch):
-        dep = oracle.depths(case.local_parent(b))
+        dep = node_depths(case.local_parent(b))
         visible += int(case.prefix_len[b]) * len(dep) + int(dep.sum())
     flops = 4.0 * d * hq * visible
     return bytes_, flops
@@ -355,6 +364,8 @@ def measure_draft_tree(tv, case, reps: int) -> dict:
                 note="one wavefront per sequence; draws are serial within a sequence")
 
 
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -364,67 +375,105 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(case, budget_s: float = 10.0):
-    """The oracle, as it stands, on whole steps of the workload until ~budget_s."""
+def one_sequence(case, b: int):
+    """Sequence b of a case as a batch of one (the paged pool stays shared)."""
+    n0, n1 = int(case.cu_nodes[b]), int(case.cu_nodes[b + 1])
+    sl = slice(n0, n1)
+    return dict(q=case.q[sl], k_tree=case.k_tree[sl], v_tree=case.v_tree[sl],
+                block_table=case.block_table[b:b + 1], prefix_len=case.prefix_len[b:b + 1],
+                cu_nodes=np.array([0, n1 - n0], dtype=np.int32), parent=case.parent[sl],
+                p_target=case.p_target[sl], p_draft=case.p_draft[sl], token=case.token[sl],
+                u_accept=case.u_accept[sl], u_resample=case.u_resample[sl])
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the workload: whole verify
+    steps (index + attention + acceptance) of one sequence at a time, cycling
+    through the batch, until about budget_s (at least one sequence)."""
     import oracle
     import workloads as W
     f = lambda a: W.to_f64(a, case.dtype)
-    args = (f(case.q), f(case.k_cache), f(case.v_cache))
-    kt, vt = f(case.k_tree), f(case.v_tree)
-    steps, t0 = 0, time.perf_counter()
+    kc, vc = f(case.k_cache), f(case.v_cache)
+    seqs, tokens, t0 = 0, 0, time.perf_counter()
     while True:
-        oracle.build_index(case.parent, case.cu_nodes, max(1, case.max_nodes), case.prefix_len)
-        oracle.tree_attention(*args, case.block_table, case.prefix_len, kt, vt, case.cu_nodes,
-                              case.parent, case.hq, case.hkv, case.scale)
-        oracle.accept(case.p_target, case.p_draft, case.token, case.u_accept, case.u_resample,
-                      case.parent, case.cu_nodes, case.vocab, 16)
-        steps += 1
+        s = one_sequence(case, seqs % case.batch)
+        n = int(s["cu_nodes"][-1])
+        oracle.build_index(s["parent"], s["cu_nodes"], max(1, n), s["prefix_len"])
+        oracle.tree_attention(f(s["q"]), kc, vc, s["block_table"], s["prefix_len"], f(s["k_tree"]),
+                              f(s["v_tree"]), s["cu_nodes"], s["parent"], case.hq, case.hkv,
+                              case.scale)
+        oracle.accept(s["p_target"], s["p_draft"], s["token"], s["u_accept"], s["u_resample"],
+                      s["parent"], s["cu_nodes"], case.vocab, 16)
+        seqs += 1
+        tokens += n
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 1000:
+        if el >= budget_s or seqs >= 1000:
             break
-    return dict(value=case.total_nodes * steps / el, unit="tokens/s", cores=blas_threads(),
-                kind="oracle",
-                sample=f"{steps} whole verify steps of the same workload (index + attention + "
-                       f"acceptance) in {el:.1f} s; fp64 numpy BLAS + Python loops")
+    whole = seqs // case.batch
+    sample = (f"{seqs} sequence-steps ({whole} whole batch steps + {seqs % case.batch} sequences)"
+              if case.batch > 1 else f"{seqs} whole verify steps")
+    return dict(value=round(tokens / el, 2), unit="tokens/s", cores=blas_threads(),
+                host_cpus=os.cpu_count(), kind="oracle",
+                sample=f"{sample} of this workload, {tokens} tree tokens in {el:.1f} s: "
+                       "index + attention + acceptance per sequence; fp64 numpy (BLAS threads = "
+                       "cores) + Python loops")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--seed", type=int, default=1234)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--kernel-reps", type=int, default=50)
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run a plain copy of a known size first (for counter scaling)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
-                    help="write the traffic summary for --config from two counter passes")
-    args = ap.parse_args()
-    if args.summarize_pmc:
-        summarize_pmc(args.config, *args.summarize_pmc)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
-        sys.exit(2)
+def graph_time_us(torch, fn, reps: int, trials: int = 5) -> float:
+    """Median over `trials` replays of a graph of `reps` back-to-back calls of fn,
+    timed with events on the replay stream; microseconds per call."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(trials):
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        times.append(s_ev.elapsed_time(e_ev) / reps)
+    del g
+    return float(np.median(times)) * 1e3
 
-    import torch
-    import tree_attention_verification_04_amd as tv
+
+def roofline(case, config: int, attn_us: float) -> dict:
+    """Bound, achieved rate and fraction of the attention call against its roof."""
     import workloads as W
+    bytes_, flops = attention_cost(case)
+    if case.dtype == W.DT_F32:
+        t_mem, t_cmp = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (VALU_FP32_PEAK_TFS * 1e12)
+        cbound, cpeak = "alu", VALU_FP32_PEAK_TFS
+    else:
+        t_mem, t_cmp = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)
+        cbound, cpeak = "mfma", MFMA_BF16_PEAK_TFS
+    gbs = bytes_ / (attn_us * 1e-6) / 1e9
+    if t_mem >= t_cmp:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        ach = flops / (attn_us * 1e-6) / 1e12
+        roof = dict(bound=cbound, achieved=round(ach, 2), peak=cpeak, unit="TFLOP/s",
+                    frac=round(ach / cpeak, 4), hbm_GBps=round(gbs, 1))
+    traffic = recorded_traffic(config)
+    roof["traffic"] = traffic
+    roof["traffic_over_alg_bytes"] = round(traffic / bytes_, 3) if traffic else None
+    roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
+                alg_bytes=int(bytes_), alg_flops=float(flops))
+    return roof
 
-    tv.load()
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.add(src, 1.0, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
-        torch.cuda.synchronize()
-        del src, dst
-    case = W.make_config(args.config, args.seed)
+
+def measure_workload(torch, tv, config: int, args, headline: bool) -> dict:
+    """Step, attention call and side rows of one workload on the GPU, plus its CPU
+    baseline.  The headline workload gets every side row; the others the FP8 variant."""
+    import workloads as W
+    t_gen = time.perf_counter()
+    case = W.make_config(config, args.seed)
     dev = W.case_to_device(case, "cuda:0")
+    t_gen = time.perf_counter() - t_gen
     mn = max(1, case.max_nodes)
     words = (mn + 63) // 64
     total, batch = case.total_nodes, case.batch
@@ -437,7 +486,7 @@ def main():
     ws_a = tv.tree_verify_attention_workspace_size(batch, total, mn, case.max_prefix, case.hq,
                                                    case.hkv, case.d, dt)
     ws_attn = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device="cuda")
-    ws_acc = torch.empty(max(tv.tree_accept_workspace_size(batch, case.vocab), 1), dtype=torch.uint8,
+    ws_acc = torch.zeros(max(tv.tree_accept_workspace_size(batch, case.vocab), 1), dtype=torch.uint8,
                          device="cuda")
     acc_out = dict(accept_len=torch.empty(batch, dtype=torch.int32, device="cuda"),
                    path=torch.empty((batch, max_path), dtype=torch.int32, device="cuda"),
@@ -458,21 +507,22 @@ def main():
                        dev["u_resample"], dev["parent"], dev["cu_nodes"], mn, max_path,
                        outputs=acc_out, workspace=ws_acc, err=err)
 
+    steps = args.steps if headline else min(args.steps, args.other_steps)
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
     if int(err.item()) != 0:
-        raise SystemExit(f"device error word {int(err.item())}")
+        raise SystemExit(f"workload {config}: device error word {int(err.item())}")
 
     # eager rate (host launch overhead included)
     t0 = time.perf_counter()
-    n_eager = min(args.steps, 200)
+    n_eager = min(steps, 100)
     for _ in range(n_eager):
         step()
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
 
-    # graph-captured step
+    # graph-captured step, K replays between two events (synchronised on both sides)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -487,92 +537,127 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         graph.replay()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = start.elapsed_time(end) / steps
+    del graph
     if int(err.item()) != 0:
-        raise SystemExit(f"device error word {int(err.item())}")
+        raise SystemExit(f"workload {config}: device error word {int(err.item())}")
 
-    # attention alone: back-to-back launches in one graph, timed with events on its stream
-    reps = args.kernel_reps
-    g_attn = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_attn):
-        for _ in range(reps):
-            attention()
-    g_attn.replay()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(5):
-        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_ev.record()
-        g_attn.replay()
-        e_ev.record()
-        torch.cuda.synchronize()
-        times.append(s_ev.elapsed_time(e_ev) / reps)
-    attn_us = float(np.median(times)) * 1e3
-
-    bytes_, flops = attention_cost(case)
-    if case.dtype == W.DT_F32:
-        t_mem, t_cmp = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (VALU_FP32_PEAK_TFS * 1e12)
-        cbound, cpeak = "alu", VALU_FP32_PEAK_TFS
-    else:
-        t_mem, t_cmp = bytes_ / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)
-        cbound, cpeak = "mfma", MFMA_BF16_PEAK_TFS
-    if t_mem >= t_cmp:
-        ach = bytes_ / (attn_us * 1e-6) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
-    else:
-        ach = flops / (attn_us * 1e-6) / 1e12
-        roof = dict(bound=cbound, achieved=round(ach, 2), peak=cpeak, unit="TFLOP/s",
-                    frac=round(ach / cpeak, 4), traffic=None)
-    roof["traffic"] = recorded_traffic(args.config)
-    roof.update(kernel="tree_verify_attention", us_per_launch=round(attn_us, 3),
-                alg_bytes=int(bytes_), alg_flops=float(flops),
-                measured_copy_GBps=measured_copy_gbps(torch))
-
-    # the step's outcome (the same every step: fixed inputs): tokens it accepts, the
-    # accepted paths plus the resampled tokens, as context beside the verified rate
+    # attention alone: back-to-back launches in one graph, timed on its stream
+    attn_us = graph_time_us(torch, attention, args.kernel_reps)
+    roof = roofline(case, config, attn_us)
     torch.cuda.synchronize()
     accepted = int(acc_out["accept_len"].sum().item()) + int((acc_out["resample_token"] >= 0).sum().item())
-    commit = measure_commit(tv, case, dev, acc_out, max_path, reps)
-    softmax = measure_softmax(tv, case, reps)
-    fp8 = measure_fp8(tv, case, dev, anc, mn, attn_us, reps)
-    draft = measure_draft_tree(tv, case, reps)
+    res = dict(workload=W.CONFIG_NAMES[config], steps=steps, ms_per_step=round(ms_step, 5),
+               us_per_step=round(ms_step * 1e3, 2), us_per_step_eager=round(eager_ms * 1e3, 2),
+               tokens_per_s=round(total / (ms_step * 1e-3), 1), attention_us=round(attn_us, 3),
+               roofline=roof,
+               config={"workload": W.CONFIG_NAMES[config], "batch": batch, "tree_nodes": total,
+                       "max_prefix": case.max_prefix, "hq": case.hq, "hkv": case.hkv,
+                       "head_dim": case.d, "vocab": case.vocab},
+               accepted={"tokens_per_step": accepted,
+                         "tokens_per_s": round(accepted / (ms_step * 1e-3), 1)},
+               wall_s=round(wall, 3), input_gen_s=round(t_gen, 1),
+               dtype="bf16" if case.dtype == W.DT_BF16 else "f32")
+    fp8 = measure_fp8(tv, case, dev, anc, mn, attn_us, args.kernel_reps)
+    if headline:
+        res["next_rows"] = {"kv_commit": measure_commit(tv, case, dev, acc_out, max_path, args.kernel_reps),
+                            "softmax_rows": measure_softmax(tv, case, args.kernel_reps),
+                            "fp8_kv_attention": fp8,
+                            "draft_tree": measure_draft_tree(tv, case, args.kernel_reps)}
+        res["measured_copy_GBps"] = measured_copy_gbps(torch)
+    elif fp8 is not None:
+        res["fp8_kv_attention"] = fp8
+    del dev, anc, depth, out, ws_attn, ws_acc, acc_out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(f"# workload {config} done: step {res['us_per_step']} us, attention {attn_us:.2f} us",
+          file=sys.stderr, flush=True)
+    return res
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--other-steps", type=int, default=200, help="steps timed per other workload")
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain copy of a known size first (for counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write the traffic summary for --config from two counter passes")
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.config, *args.summarize_pmc)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; the verify path is "
+                                   "measured on one GPU's share (--gpus must be 1)"}))
+        sys.exit(2)
+
+    import torch
+    import tree_attention_verification_04_amd as tv
+
+    tv.load()
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)  # an elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
+    head = measure_workload(torch, tv, args.config, args, headline=True)
+    others = {}
+    if not args.only:
+        for c in range(5):
+            if c != args.config:
+                r = measure_workload(torch, tv, c, args, headline=False)
+                others[r["workload"].split(":")[0]] = r
+
+    cfg = dict(head["config"])
+    cfg.update(step="tree_build_index + tree_verify_attention + tree_accept",
+               timing="HIP-graph replay, events on the launch stream", wall_s=head["wall_s"])
+    roof = dict(head["roofline"])
+    roof["measured_copy_GBps"] = head["measured_copy_GBps"]
     res = {
         "metric": "verified tree tokens/s",
-        "value": round(total / (ms_step * 1e-3), 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "us_per_step": round(ms_step * 1e3, 2),
-        "us_per_step_eager": round(eager_ms * 1e3, 2),
+        "ms_per_step": head["ms_per_step"],
+        "us_per_step": head["us_per_step"],
+        "us_per_step_eager": head["us_per_step_eager"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if case.dtype == W.DT_BF16 else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded, HBM-resident; pages' datasets and models are not used)",
-        "config": {"workload": W.CONFIG_NAMES[args.config], "batch": batch, "tree_nodes": total,
-                   "max_prefix": case.max_prefix, "hq": case.hq, "hkv": case.hkv, "head_dim": case.d,
-                   "vocab": case.vocab, "step": "tree_build_index + tree_verify_attention + tree_accept",
-                   "timing": "HIP-graph replay, events on the launch stream",
-                   "wall_s": round(wall, 3)},
+        "config": cfg,
         "roofline": roof,
-        "accepted": {"tokens_per_step": accepted,
-                     "tokens_per_s": round(accepted / (ms_step * 1e-3), 1),
-                     "note": "accepted path lengths + resampled tokens; the synthetic target "
-                             "and draft rows are independent draws, not a model's"},
-        "next_rows": {"kv_commit": commit, "softmax_rows": softmax, "fp8_kv_attention": fp8,
-                      "draft_tree": draft},
+        "attention_us": head["attention_us"],
+        "accepted": dict(head["accepted"], note="accepted path lengths + resampled tokens; the "
+                         "synthetic target and draft rows are independent draws, not a model's"),
+        "next_rows": head["next_rows"],
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if "cpu_baseline" in head:
+        res["cpu_baseline"] = head["cpu_baseline"]
+    if others:
+        res["other_workloads"] = others
     print(json.dumps(res), flush=True)
 
 

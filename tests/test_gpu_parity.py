@@ -158,7 +158,7 @@ def test_attention_tail_pieces(gpu_lib, name):
 
 
 COUNTER_CASES = {
-    # 16 prefix splits merged in the kernel (tickets)
+    # 16 prefix splits merged by the split-merge kernel
     "splits16": ([W.tree_random(np.random.default_rng(9), 200, 8)], [8000], 8, 2),
     # persistent launch with tail pieces (queue heads, exit count, tickets)
     "persistent_tail": TAIL_CASES["pieces2"][:4],
@@ -272,10 +272,15 @@ def test_attention_max_node_cap(gpu_lib):
 
 @pytest.mark.parametrize("index", [1, 2, 3, 4])
 def test_attention_full_configs(gpu_lib, index):
-    """The four bf16 verify workloads at full size, on sampled nodes."""
+    """The four bf16 verify workloads at full size, in the launch configuration the
+    benchmark times: every node of the LLaVA-like tree; first, last and random nodes
+    (all heads) of every sequence of the others."""
     case = W.make_config(index, with_probs=False)
-    seqs = None if case.batch <= 8 else {0, 7, 31, 63}
-    check_attention(gpu_lib, case, TOL_BF16, nodes=sample_nodes(case, 12, seed=index, seqs=seqs))
+    if index == 1:
+        nodes = None
+    else:
+        nodes = sample_nodes(case, 12 if case.batch <= 8 else 2, seed=index)
+    check_attention(gpu_lib, case, TOL_BF16, nodes=nodes)
 
 
 def test_attention_repeatable(gpu_lib):
@@ -345,6 +350,85 @@ def test_accept_large_vocab_bitexact(gpu_lib, vocab):
     case.p_target[same] = case.p_draft[same]
     dev = W.case_to_device(case)
     assert_accept_equal(gpu_accept(gpu_lib, case, dev, 8), oracle_accept(case, 8))
+
+
+def own_rows_for(case, seed: int, frac: float = 0.8):
+    """Own-context rows for bonus tokens: node i reads row i of a fresh set of
+    probability rows with probability frac, else -1 (no row)."""
+    rng = np.random.default_rng(seed)
+    own_row = np.where(rng.random(case.total_nodes) < frac, np.arange(case.total_nodes), -1)
+    return W.prob_rows(seed, 7, case.total_nodes, case.vocab), own_row.astype(np.int32)
+
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+def test_accept_bonus_configs_bitexact(gpu_lib, index):
+    """Bonus tokens on the five workloads: p_target = p_draft on ~90% of nodes, so
+    many accepted paths end at leaves and draw from their own-context rows (80% of
+    nodes have one); single-kernel and chunked vocabularies."""
+    case = W.make_config(index)
+    rng = np.random.default_rng(50 + index)
+    same = rng.random(case.total_nodes) < 0.9
+    case.p_target[same] = case.p_draft[same]
+    own = own_rows_for(case, 60 + index)
+    dev = W.case_to_device(case)
+    want = oracle_accept(case, 16, own)
+    got = gpu_accept(gpu_lib, case, dev, 16, own=own)
+    assert_accept_equal(got, want)
+    bonus = [b for b in range(case.batch)
+             if want["accept_len"][b] > 0 and want["resample_node"][b] == want["path"][b][want["accept_len"][b] - 1]]
+    assert bonus or case.batch == 1
+
+
+def test_accept_bonus_exhaustive_patterns_batched(gpu_lib):
+    """Every accept pattern of a 9-node tree with a point-mass own row per node: the
+    bonus is drawn exactly when the winner is a leaf (its token names the node)."""
+    par = W.tree_random(np.random.default_rng(3), 9, 4)
+    n, vocab = 9, 16
+    pats = 1 << n
+    case = W.make_case("patb", [par] * pats, [0] * pats, 1, 1, 64, W.DT_F32, vocab, 2,
+                       with_probs=False)
+    pt = np.full((n * pats, vocab), 1.0 / vocab, np.float32)
+    for m in range(pats):
+        for i in range(n):
+            if not (m >> i) & 1:
+                pt[m * n + i, 0] = 0.0       # the drafted token 0 has no target mass
+    case.p_target, case.p_draft = pt, np.full_like(pt, 1.0 / vocab)
+    case.token = np.zeros(n * pats, np.int32)
+    case.u_accept = np.full(n * pats, 0.5, np.float32)
+    case.u_resample = W.grid_uniforms(np.random.default_rng(1), n * pats)
+    own = np.zeros((n, vocab), np.float32)
+    own[np.arange(n), np.arange(n) + 1] = 1.0
+    own_row = np.tile(np.arange(n, dtype=np.int32), pats)
+    dev = W.case_to_device(case)
+    want = oracle_accept(case, n, (own, own_row))
+    assert_accept_equal(gpu_accept(gpu_lib, case, dev, n, own=(own, own_row)), want)
+    leaf_wins = sum(1 for m in range(pats) if want["resample_token"][m] == want["resample_node"][m] + 1)
+    assert leaf_wins > 0
+
+
+@pytest.mark.parametrize("vocab", [1000, 65537, 131072])
+def test_accept_bonus_errors(gpu_lib, vocab):
+    """Bonus rows outside [-1, own_rows), a bad uniform at the leaf and an all-zero own
+    row: the same error bits and outputs as the oracle, in both launch shapes."""
+    parents = [W.tree_chain(3)] * 5
+    case = W.make_case("bonerr", parents, [0] * 5, 1, 1, 64, W.DT_F32, vocab, 12)
+    case.p_target[:] = case.p_draft          # every chain accepted to its leaf
+    own_rows = 4
+    p_own = W.prob_rows(3, 9, own_rows, vocab)
+    p_own[3] = 0.0
+    own_row = np.full(case.total_nodes, -1, np.int32)
+    leaf = [3 * b + 2 for b in range(5)]
+    own_row[leaf] = [1, own_rows, 3, 2, -2]  # ok, past the rows, zero row, ok (bad u), negative
+    case.u_resample[leaf[3]] = 1.0
+    dev = W.case_to_device(case)
+    ws = torch.zeros(max(1, gpu_lib.tree_accept_workspace_size(5, vocab)), dtype=torch.uint8,
+                     device="cuda")
+    want = oracle_accept(case, 4, (p_own, own_row))
+    assert want["err"] == oracle.ERR_ZERO_MASS | oracle.ERR_UNIFORM | 128
+    for _ in range(2):
+        assert_accept_equal(gpu_accept(gpu_lib, case, dev, 4, own=(p_own, own_row), workspace=ws),
+                            want)
+        assert int(ws[:256].count_nonzero().item()) == 0   # ticket words left zero
 
 
 def test_accept_error_words(gpu_lib):
