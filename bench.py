@@ -500,12 +500,15 @@ def measure_workload(torch, tv, config: int, args, headline: bool) -> dict:
                                  anc, mn, case.max_prefix, out=out, want_lse=False,
                                  workspace=ws_attn if ws_a else None, err=err)
 
-    def step():
-        tv.tree_build_index(dev["parent"], dev["cu_nodes"], mn, anc=anc, depth=depth, err=err)
-        attention()
+    def accept():
         tv.tree_accept(dev["p_target"], dev["p_draft"], dev["token"], dev["u_accept"],
                        dev["u_resample"], dev["parent"], dev["cu_nodes"], mn, max_path,
                        outputs=acc_out, workspace=ws_acc, err=err)
+
+    def step():
+        tv.tree_build_index(dev["parent"], dev["cu_nodes"], mn, anc=anc, depth=depth, err=err)
+        attention()
+        accept()
 
     steps = args.steps if headline else min(args.steps, args.other_steps)
     for _ in range(max(1, args.warmup)):
@@ -549,12 +552,14 @@ def measure_workload(torch, tv, config: int, args, headline: bool) -> dict:
 
     # attention alone: back-to-back launches in one graph, timed on its stream
     attn_us = graph_time_us(torch, attention, args.kernel_reps)
+    accept_us = graph_time_us(torch, accept, args.kernel_reps)
     roof = roofline(case, config, attn_us)
     torch.cuda.synchronize()
     accepted = int(acc_out["accept_len"].sum().item()) + int((acc_out["resample_token"] >= 0).sum().item())
     res = dict(workload=W.CONFIG_NAMES[config], steps=steps, ms_per_step=round(ms_step, 5),
                us_per_step=round(ms_step * 1e3, 2), us_per_step_eager=round(eager_ms * 1e3, 2),
                tokens_per_s=round(total / (ms_step * 1e-3), 1), attention_us=round(attn_us, 3),
+               accept_us=round(accept_us, 3),
                roofline=roof,
                config={"workload": W.CONFIG_NAMES[config], "batch": batch, "tree_nodes": total,
                        "max_prefix": case.max_prefix, "hq": case.hq, "hkv": case.hkv,
@@ -650,6 +655,7 @@ def main():
         "config": cfg,
         "roofline": roof,
         "attention_us": head["attention_us"],
+        "accept_us": head["accept_us"],
         "accepted": dict(head["accepted"], note="accepted path lengths + resampled tokens; the "
                          "synthetic target and draft rows are independent draws, not a model's"),
         "next_rows": head["next_rows"],

@@ -221,10 +221,10 @@ int tree_draft_build(const float* probs, const float* u, int32_t batch, int32_t 
                      void* stream);
 
 /*
- * tree_accept — fused acceptance for every sequence, no host round-trip
- * ([P537] §2.2.3: per-node p_accept = min(1, p_target / p_draft), one uniform
- * per node, depth-first walk from the root cut at the first rejected node,
- * longest accepted path, sampling fused with the traversal; [P525] §1.2:
+ * tree_accept — fused acceptance for every sequence, one launch, no host
+ * round-trip ([P537] §2.2.3: per-node p_accept = min(1, p_target / p_draft), one
+ * uniform per node, depth-first walk from the root cut at the first rejected
+ * node, longest accepted path, sampling fused with the traversal; [P525] §1.2:
  * resample at the rejection point).
  *
  * Per sequence:
@@ -236,30 +236,45 @@ int tree_draft_build(const float* probs, const float* u, int32_t batch, int32_t 
  *   accept_len   depth(w), 0 if none; path[0 .. accept_len-1] = the root-level
  *                ancestor of w down to w (local ids), the rest -1
  *   rejection    c = smallest-index child of w (w = -1: smallest-index node
- *                under the prefix); none if w has no child -> -1 outputs
+ *                under the prefix)
  *   resample     token drawn from norm(max(0, pt_c - pd_c)), or from pt_c when
  *                that has no mass, by an integer inverse CDF: q_k =
  *                floor(((double)pt - (double)pd) * 2^40) for positive
  *                differences, Z = sum q_k, T = floor(u_resample[c] * Z)
  *                (exact), token = smallest k with q_0 + .. + q_k > T.
  *                Integer sums make the token independent of summation order.
+ *   bonus        when w has no child (the whole path to a leaf passed) and
+ *                own_row[w] >= 0: token drawn from p_own[own_row[w]] (p_target at
+ *                w's own context: the one forward pass over the tree gives it,
+ *                [P537] §2.2.3) with u_resample[w], same integer inverse CDF on
+ *                q_k = floor((double)p_own_k * 2^40); resample_node = w.  Without
+ *                own_row (NULL), or own_row[w] = -1, nothing: -1 outputs.
  *
  *   p_target/p_draft [total_nodes, vocab] float: row i = the two distributions
  *                that judged node i's drafted token (those at its parent's context)
  *   token        [total_nodes] int32; u_accept/u_resample [total_nodes] float in [0, 1)
  *   parent, cu_nodes as for tree_build_index; max_nodes <= TV_MAX_NODES
+ *   p_own        [own_rows, vocab] float or NULL: target rows at nodes' own contexts
+ *   own_row      [total_nodes] int32 or NULL: row of p_own at node i's own context,
+ *                -1 = none (only the winner's entry is read)
  *   accept_len   out [batch] int32; path out [batch, max_path] int32
- *   resample_node, resample_token out [batch] int32 (-1 = none)
+ *   resample_node out [batch] int32: c (residual), w (bonus) or -1
+ *   resample_token out [batch] int32 (-1 = none)
  *   node_ok      out [total_nodes] uint8 or NULL
- *   workspace    >= tree_accept_workspace_size(batch, vocab) bytes
+ *   workspace    vocab <= 65536: unused (may be NULL); larger vocabularies: at least
+ *                tree_accept_workspace_size(batch, vocab) bytes, zero-filled before its
+ *                first use (every call leaves its ticket words zero again); calls that
+ *                share one workspace must not overlap on the device
  *   err          TV_ERR_BAD_PARENT, TV_ERR_TOO_MANY_NODES, TV_ERR_TOKEN, TV_ERR_ZERO_MASS,
- *                TV_ERR_PATH, TV_ERR_UNIFORM
+ *                TV_ERR_PATH, TV_ERR_UNIFORM, TV_ERR_ROW (own_row[w] outside
+ *                [-1, own_rows): no bonus)
  */
 size_t tree_accept_workspace_size(int32_t batch, int32_t vocab);
 
 int tree_accept(const float* p_target, const float* p_draft, const int32_t* token,
                 const float* u_accept, const float* u_resample, const int32_t* parent,
-                const int32_t* cu_nodes, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                const int32_t* cu_nodes, const float* p_own, const int32_t* own_row,
+                int32_t own_rows, int32_t batch, int32_t total_nodes, int32_t max_nodes,
                 int32_t vocab, int32_t max_path, int32_t* accept_len, int32_t* path,
                 int32_t* resample_node, int32_t* resample_token, uint8_t* node_ok,
                 void* workspace, size_t workspace_bytes, int32_t* err, void* stream);

@@ -56,17 +56,24 @@ def rows_of(case: W.Case, nodes):
                            for b in range(case.batch)]).astype(np.int64)
 
 
-def gpu_accept(tv, case: W.Case, dev, max_path: int, max_nodes=None):
+def gpu_accept(tv, case: W.Case, dev, max_path: int, max_nodes=None, own=None, workspace=None):
+    """tree_accept on the device; own = (p_own, own_row) numpy arrays for bonus tokens."""
     mn = max_nodes or max_nodes_of(case)
+    kw = {}
+    if own is not None:
+        kw = dict(p_own=torch.from_numpy(np.ascontiguousarray(own[0])).cuda(),
+                  own_row=torch.from_numpy(np.ascontiguousarray(own[1], dtype=np.int32)).cuda())
     o = tv.tree_accept(dev["p_target"], dev["p_draft"], dev["token"], dev["u_accept"],
-                       dev["u_resample"], dev["parent"], dev["cu_nodes"], mn, max_path)
+                       dev["u_resample"], dev["parent"], dev["cu_nodes"], mn, max_path,
+                       workspace=workspace, **kw)
     torch.cuda.synchronize()
     return {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in o.items()}
 
 
-def oracle_accept(case: W.Case, max_path: int):
+def oracle_accept(case: W.Case, max_path: int, own=None):
+    p_own, own_row = own if own is not None else (None, None)
     return oracle.accept(case.p_target, case.p_draft, case.token, case.u_accept, case.u_resample,
-                         case.parent, case.cu_nodes, case.vocab, max_path)
+                         case.parent, case.cu_nodes, case.vocab, max_path, p_own, own_row)
 
 
 def assert_accept_equal(got: dict, want: dict):

@@ -173,13 +173,13 @@ def test_draft_build_host_checks(lib):
 
 def test_accept_host_checks(lib):
     one = ctypes.c_void_p(16)
-    need = lib.tree_accept_workspace_size(2, 1000)
-    assert need >= 2 * 4 * 1 + 16
+    need = lib.tree_accept_workspace_size(2, 100000)
+    assert need >= 256 + 2 * 25 * 16          # tickets, then 25 chunks of 4096 entries
 
     def call(**kw):
-        a = dict(pt=one, pd=one, tok=one, ua=one, ur=one, par=one, cu=one, batch=2, total=5,
-                 max_nodes=4, vocab=1000, max_path=4, alen=one, path=one, rn=one, rt=one,
-                 ok=None, ws=one, ws_bytes=need, err=one, stream=None)
+        a = dict(pt=one, pd=one, tok=one, ua=one, ur=one, par=one, cu=one, own=None, own_row=None,
+                 own_rows=0, batch=2, total=5, max_nodes=4, vocab=100000, max_path=4, alen=one,
+                 path=one, rn=one, rt=one, ok=None, ws=one, ws_bytes=need, err=one, stream=None)
         a.update(kw)
         return lib.tree_accept(*a.values())
 
@@ -188,6 +188,9 @@ def test_accept_host_checks(lib):
     assert call(max_nodes=5000) == tv.TV_EUNSUPPORTED
     assert call(ws_bytes=need - 1) == tv.TV_EWORKSPACE
     assert call(ws=None) == tv.TV_EWORKSPACE
+    assert call(own_row=one, own_rows=3) == tv.TV_EINVAL      # own rows without p_own
+    assert call(own_rows=-1) == tv.TV_EINVAL
+    assert b"tree_accept" in lib.tree_last_error()
     assert call(pt=None) == tv.TV_EINVAL
     assert call(path=None) == tv.TV_EINVAL
     assert call(batch=0) == tv.TV_OK

@@ -77,7 +77,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_draft_build.restype = ctypes.c_int
     lib.tree_accept_workspace_size.argtypes = [I, I]
     lib.tree_accept_workspace_size.restype = Z
-    lib.tree_accept.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P, P]
+    lib.tree_accept.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
+                                Z, P, P]
     lib.tree_accept.restype = ctypes.c_int
     lib.tree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, I, P, I, P, P, P]
     lib.tree_commit_kv.restype = ctypes.c_int
@@ -338,10 +339,16 @@ def tree_accept_workspace_size(batch: int, vocab: int) -> int:
 
 
 def tree_accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes: int,
-                max_path: int, *, node_ok=True, outputs: dict | None = None, workspace=None,
-                err=None, stream=None) -> dict:
+                max_path: int, *, p_own=None, own_row=None, node_ok=True,
+                outputs: dict | None = None, workspace=None, err=None, stream=None) -> dict:
     """Ratio test, longest accepted path and residual resample for every sequence.
 
+    p_own [R, vocab] float32 / own_row [total] int32 (optional, together): target
+    rows at each node's own context (-1 = none); a path that ends at a leaf then
+    draws its bonus token from the leaf's row.
+    workspace: a uint8 device tensor of at least tree_accept_workspace_size bytes,
+    zero-filled before its first use (every call leaves its ticket words zero); a
+    zeroed one is allocated when none is given.
     Returns dict(accept_len [B], path [B, max_path], resample_node [B],
     resample_token [B], node_ok [total] uint8 or None, err [1]).
     """
@@ -355,6 +362,15 @@ def tree_accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes
     total, vocab = p_target.shape
     if tuple(p_draft.shape) != (total, vocab):
         raise ValueError("p_draft must match p_target")
+    if (p_own is None) != (own_row is None):
+        raise ValueError("p_own and own_row go together")
+    own_rows = 0
+    if p_own is not None:
+        _need(p_own, "p_own", torch.float32, 2)
+        _need(own_row, "own_row", torch.int32, 1)
+        if p_own.shape[1] != vocab or own_row.numel() != total:
+            raise ValueError("p_own must be [rows, vocab] and own_row [total_nodes]")
+        own_rows = p_own.shape[0]
     batch = cu_nodes.numel() - 1
     dev = p_target.device
     o = outputs if outputs is not None else {}
@@ -366,13 +382,14 @@ def tree_accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes
         o["node_ok"] = torch.empty(total, dtype=torch.uint8, device=dev) if node_ok else None
     need = tree_accept_workspace_size(batch, vocab)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)  # kept zero
     err = _err_word(err, dev)
     o["err"] = err
     _check("tree_accept",
            lib.tree_accept(_ptr(p_target), _ptr(p_draft), _ptr(token), _ptr(u_accept),
-                           _ptr(u_resample), _ptr(parent), _ptr(cu_nodes), batch, total,
-                           max_nodes, vocab, max_path, _ptr(o["accept_len"]), _ptr(o["path"]),
+                           _ptr(u_resample), _ptr(parent), _ptr(cu_nodes), _ptr(p_own),
+                           _ptr(own_row), own_rows, batch, total, max_nodes, vocab, max_path,
+                           _ptr(o["accept_len"]), _ptr(o["path"]),
                            _ptr(o["resample_node"]), _ptr(o["resample_token"]),
                            _ptr(o.get("node_ok")), _ptr(workspace),
                            workspace.numel(), _ptr(err), _stream(stream)))

@@ -4,37 +4,64 @@
 // 机制与显存碎片整理联合加速" (ufo.work/2026/537), §2.2.3: each node's acceptance
 // probability min(1, p_target / p_draft) at its drafted token, one uniform per node,
 // a depth-first walk from the root that stops below the first rejected node, and the
-// longest accepted path, all inside GPU kernels.  At the rejection point a token is
+// longest accepted path, all inside one GPU kernel.  At the rejection point a token is
 // resampled (page "端侧大模型推测解码草稿模型动态剪枝策略：详解基于重要性采样的树形验证并行加速
 // 机制" (ufo.work/2026/525), §1.2) from norm(max(0, p_target - p_draft)), falling back
-// to p_target itself when that has no mass (same page, §7.2).
+// to p_target itself when that has no mass (same page, §7.2).  When the path ends at
+// a leaf and the caller passes the target distribution at that leaf's own context
+// (the one forward pass over the tree gives one at every node, page 537 §2.2.3), the
+// extra token is drawn from it instead: the bonus token.
 //
-// Up to 65536 vocabulary entries one kernel does everything (the walk's workgroup
-// scans the rejection row); for larger vocabularies three kernels on the stream:
-//   k_accept_walk    one workgroup per sequence: ratio tests, ancestor walks, the
-//                    deepest accepted node (ties: smallest index), the path, and the
-//                    rejection node c (smallest-index child of the winner).
-//   k_resid_partial  (vocab chunk, sequence) workgroups: integer residual weights
-//                    of row c summed per chunk.
-//   k_resid_select   one workgroup per sequence: total mass, exact threshold, the
-//                    chunk and then the element where the running sum passes it.
-// The weights are integers (floor of the fp64 difference times 2^40), so every sum
-// is exact and the token does not depend on how the vocabulary is split.
+// One launch per call.  Up to 65536 vocabulary entries, one workgroup per sequence
+// walks the tree and scans the row it samples.  Above that, there is a workgroup per
+// (sequence, vocabulary chunk), all chunks of a sequence on one die: every workgroup
+// of a sequence repeats the walk (a few hundred gathered floats, cached in the die's
+// L2 after the first), sums the integer weights of its chunk of
+// the sampled row, publishes them and takes a ticket; the workgroup that takes the
+// sequence's last ticket finds the chunk and then the element where the running sum
+// passes the threshold.  No workgroup waits for another.  The weights are integers
+// (floor of the fp64 difference times 2^40), so every sum is exact and the token does
+// not depend on how the vocabulary is split.
 #include <limits.h>
 
-#include "tv_common.h"
+#include <cstdio>
+
+#include "accept.h"
 
 namespace tv {
+
+namespace {
 
 constexpr int kAcceptThreads = 256;
 constexpr int kResidChunk = 4096;                       // vocabulary entries per chunk
 constexpr int kResidPerThread = kResidChunk / kAcceptThreads;
-constexpr int kFusedVocab = 65536;  // up to this vocabulary the walk's workgroup resamples
+constexpr int kFusedVocab = kAcceptFusedVocab;  // up to this vocabulary one workgroup per sequence
 constexpr int kMaxVocab = 1 << 18;
 constexpr int kMaxResidChunks = kMaxVocab / kResidChunk;
 static_assert(kResidPerThread % 4 == 0, "whole float4 per thread");
 
 #pragma clang fp contract(off)
+
+struct AcceptArgs {
+  const float* pt;          // [total_nodes, vocab]
+  const float* pd;
+  const int32_t* token;
+  const float* u_acc;
+  const float* u_res;
+  const int32_t* parent;
+  const int32_t* cu_nodes;
+  const float* p_own;       // [own_rows, vocab] or null
+  const int32_t* own_row;   // [total_nodes] or null
+  int own_rows, max_nodes, vocab, max_path;
+  int32_t* accept_len;
+  int32_t* path;
+  int32_t* resample_node;
+  int32_t* resample_token;
+  uint8_t* node_ok;
+  int* tickets;             // [batch] finish tickets (chunked launch), zero between calls
+  uint64_t* part;           // [batch, chunks, 2] chunk sums (chunked launch)
+  int32_t* err;
+};
 
 // Fixed-point residual weight of one vocabulary entry.
 __device__ __forceinline__ uint64_t resid_weight(float pt, float pd) {
@@ -107,20 +134,28 @@ __device__ uint64_t block_sum_u64(uint64_t v) {
   return all;
 }
 
-// Residual resample of row c inside one workgroup (small vocabularies): thread t
+// weight of entry k in mode 0 (residual pt - pd) or 1 (pt alone); pd_row is null for
+// a bonus row, whose residual weights are all zero
+__device__ __forceinline__ uint64_t weight_at(const float* __restrict__ pt_row,
+                                              const float* __restrict__ pd_row, int k, int mode) {
+  if (mode == 1) return target_weight(pt_row[k]);
+  return pd_row != nullptr ? resid_weight(pt_row[k], pd_row[k]) : 0ull;
+}
+
+// Token of row (pt_row, pd_row) inside one workgroup (small vocabularies): thread t
 // sums the integer weights of its contiguous slice, a block scan over the slices
 // finds the one where the running sum passes the threshold, and that thread walks
-// its slice again.  Same integers as the multi-workgroup path, so the same token.
-__device__ void resample_in_block(const float* __restrict__ pt_row, const float* __restrict__ pd_row,
-                                  int vocab, float u, int32_t* __restrict__ out_token,
-                                  int32_t* __restrict__ err) {
+// its slice again.  Same integers as the chunked path, so the same token.
+__device__ void sample_in_block(const float* __restrict__ pt_row, const float* __restrict__ pd_row,
+                                int vocab, float u, int32_t* __restrict__ out_token,
+                                int32_t* __restrict__ err) {
   const int tid = threadIdx.x;
   const int len = ((vocab + kAcceptThreads - 1) / kAcceptThreads + 3) & ~3;
   const int k0 = min(vocab, tid * len), k1 = min(vocab, k0 + len);
   uint64_t sr = 0, st = 0;
   for (int k = k0; k < k1; ++k) {
     const float t = pt_row[k];
-    sr += resid_weight(t, pd_row[k]);
+    if (pd_row != nullptr) sr += resid_weight(t, pd_row[k]);
     st += target_weight(t);
   }
   const uint64_t zr = block_sum_u64(sr);
@@ -140,7 +175,7 @@ __device__ void resample_in_block(const float* __restrict__ pt_row, const float*
   if (local > 0 && excl <= t_thr && t_thr < excl + local) {
     uint64_t run = excl;
     for (int k = k0; k < k1; ++k) {
-      run += mode == 0 ? resid_weight(pt_row[k], pd_row[k]) : target_weight(pt_row[k]);
+      run += weight_at(pt_row, pd_row, k, mode);
       if (run > t_thr) {
         *out_token = k;
         break;
@@ -149,200 +184,57 @@ __device__ void resample_in_block(const float* __restrict__ pt_row, const float*
   }
 }
 
-template <bool kFused>
-__global__ void __launch_bounds__(kAcceptThreads) k_accept_walk(
-    const float* __restrict__ pt, const float* __restrict__ pd, const int32_t* __restrict__ token,
-    const float* __restrict__ u_acc, const float* __restrict__ u_res,
-    const int32_t* __restrict__ parent, const int32_t* __restrict__ cu_nodes, int max_nodes,
-    int vocab, int max_path, int32_t* __restrict__ accept_len, int32_t* __restrict__ path,
-    int32_t* __restrict__ resample_node, int32_t* __restrict__ resample_token,
-    uint8_t* __restrict__ node_ok, int32_t* __restrict__ ws_c, int32_t* __restrict__ err) {
-  __shared__ int16_t s_par[TV_MAX_NODES];
-  __shared__ uint8_t s_acc[TV_MAX_NODES];
-  __shared__ int s_bad, s_key, s_child, s_err, s_pending;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int n0 = cu_nodes[b];
-  const int n = cu_nodes[b + 1] - n0;
-  if (tid == 0) {
-    s_bad = 0;
-    s_key = -1;
-    s_child = INT_MAX;
-    s_err = 0;
-  }
-  for (int j = tid; j < max_path; j += kAcceptThreads) path[static_cast<long>(b) * max_path + j] = -1;
-  __syncthreads();
-  if (n > max_nodes) {
-    if (node_ok != nullptr)
-      for (int i = tid; i < n; i += kAcceptThreads) node_ok[n0 + i] = 0;
-    if (tid == 0) {
-      atomicOr(err, TV_ERR_TOO_MANY_NODES);
-      accept_len[b] = 0;
-      resample_node[b] = -1;
-      resample_token[b] = -1;
-      ws_c[b] = -1;
-    }
-    return;
-  }
-  for (int i = tid; i < n; i += kAcceptThreads) {
-    const int p = parent[n0 + i];
-    s_par[i] = static_cast<int16_t>(p);
-    if (p >= i || p < -1) s_bad = 1;
-  }
-  __syncthreads();
-  if (s_bad) {
-    if (node_ok != nullptr)
-      for (int i = tid; i < n; i += kAcceptThreads) node_ok[n0 + i] = 0;
-    if (tid == 0) {
-      atomicOr(err, TV_ERR_BAD_PARENT);
-      accept_len[b] = 0;
-      resample_node[b] = -1;
-      resample_token[b] = -1;
-      ws_c[b] = -1;
-    }
-    return;
-  }
-  // 1-2. ratio test per node: u < min(1, pt/pd)  <=>  (double)u * pd < pt for u in [0, 1)
-  int my_err = 0;
-  for (int i = tid; i < n; i += kAcceptThreads) {
-    const long g = n0 + i;
-    const int tok = token[g];
-    bool a = false;
-    if (tok < 0 || tok >= vocab) {
-      my_err |= TV_ERR_TOKEN;
-    } else {
-      const float u = u_acc[g];
-      if (!(u >= 0.0f && u < 1.0f)) {
-        my_err |= TV_ERR_UNIFORM;
-      } else {
-        const long off = g * vocab + tok;
-        a = static_cast<double>(u) * static_cast<double>(pd[off]) < static_cast<double>(pt[off]);
-      }
-    }
-    s_acc[i] = a ? 1 : 0;
-  }
-  if (my_err) atomicOr(&s_err, my_err);
-  __syncthreads();
-  // 3. a node is reached by the walk iff it and all its ancestors passed;
-  //    the winner is the reached node of largest depth, smallest index on ties
-  for (int i = tid; i < n; i += kAcceptThreads) {
-    int v = i, depth = 0;
-    bool ok = true;
-    while (v >= 0) {
-      if (!s_acc[v]) {
-        ok = false;
-        break;
-      }
-      ++depth;
-      v = s_par[v];
-    }
-    if (node_ok != nullptr) node_ok[n0 + i] = ok ? 1 : 0;
-    if (ok) atomicMax(&s_key, (depth << 12) | (4095 - i));
-  }
-  __syncthreads();
-  const int key = s_key;
-  const int w = key < 0 ? -1 : 4095 - (key & 4095);
-  const int depth_w = key < 0 ? 0 : (key >> 12);
-  // rejection point: smallest-index child of the winner (w = -1: of the prefix)
-  for (int i = tid; i < n; i += kAcceptThreads)
-    if (s_par[i] == w) atomicMin(&s_child, i);
-  __syncthreads();
-  if (tid == 0) {
-    int e = s_err;
-    accept_len[b] = depth_w;
-    int v = w;
-    for (int k = depth_w - 1; k >= 0; --k) {
-      if (k < max_path) path[static_cast<long>(b) * max_path + k] = v;
-      v = s_par[v];
-    }
-    if (depth_w > max_path) e |= TV_ERR_PATH;
-    const int c = s_child == INT_MAX ? -1 : s_child;
-    resample_node[b] = c;
-    int pending = -1;
-    if (c >= 0) {
-      const float u = u_res[n0 + c];
-      if (u >= 0.0f && u < 1.0f) pending = c;
-      else e |= TV_ERR_UNIFORM;
-    }
-    ws_c[b] = pending;
-    s_pending = pending;
-    if (pending < 0) resample_token[b] = -1;
-    if (e) atomicOr(err, e);
-  }
-  if constexpr (kFused) {
-    __syncthreads();
-    const int c = s_pending;
-    if (c < 0) return;
-    const long row = static_cast<long>(n0 + c) * vocab;
-    resample_in_block(pt + row, pd + row, vocab, u_res[n0 + c], resample_token + b, err);
-  }
-}
-
-__global__ void __launch_bounds__(kAcceptThreads) k_resid_partial(
-    const float* __restrict__ pt, const float* __restrict__ pd, const int32_t* __restrict__ cu_nodes,
-    int vocab, int chunks, const int32_t* __restrict__ ws_c, uint64_t* __restrict__ part) {
-  const int chunk = blockIdx.x, b = blockIdx.y;
-  const int c = ws_c[b];
-  if (c < 0) return;
-  const long row = static_cast<long>(cu_nodes[b] + c) * vocab;
+// Chunk `chunk` of the sampled row: sums of the residual and target weights.
+__device__ __forceinline__ void chunk_sums(const float* __restrict__ pt_row,
+                                           const float* __restrict__ pd_row, int vocab, int chunk,
+                                           uint64_t& sr, uint64_t& st) {
   const int k0 = chunk * kResidChunk;
   const int k1 = min(vocab, k0 + kResidChunk);
-  uint64_t sr = 0, st = 0;
-  const bool aligned =
-      ((vocab & 3) | ((reinterpret_cast<uintptr_t>(pt) | reinterpret_cast<uintptr_t>(pd)) & 15)) == 0;
-  if (aligned && k1 - k0 == kResidChunk) {
+  sr = 0;
+  st = 0;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(pt_row) |
+                          (pd_row != nullptr ? reinterpret_cast<uintptr_t>(pd_row) : 0);
+  if ((align & 15) == 0 && k1 - k0 == kResidChunk) {
     // whole chunk, rows 16-byte aligned: each thread takes 4 float4 of each row,
-    // all 8 loads in flight at once
-    const float4* t4 = reinterpret_cast<const float4*>(pt + row + k0);
-    const float4* d4 = reinterpret_cast<const float4*>(pd + row + k0);
-    float4 tv[kResidPerThread / 4], dv[kResidPerThread / 4];
+    // all loads in flight at once
+    const float4* t4 = reinterpret_cast<const float4*>(pt_row + k0);
+    float4 tv[kResidPerThread / 4];
 #pragma unroll
-    for (int j = 0; j < kResidPerThread / 4; ++j) {
-      tv[j] = t4[threadIdx.x + j * kAcceptThreads];
-      dv[j] = d4[threadIdx.x + j * kAcceptThreads];
+    for (int j = 0; j < kResidPerThread / 4; ++j) tv[j] = t4[threadIdx.x + j * kAcceptThreads];
+    if (pd_row != nullptr) {
+      const float4* d4 = reinterpret_cast<const float4*>(pd_row + k0);
+      float4 dv[kResidPerThread / 4];
+#pragma unroll
+      for (int j = 0; j < kResidPerThread / 4; ++j) dv[j] = d4[threadIdx.x + j * kAcceptThreads];
+#pragma unroll
+      for (int j = 0; j < kResidPerThread / 4; ++j)
+        sr += resid_weight(tv[j].x, dv[j].x) + resid_weight(tv[j].y, dv[j].y) +
+              resid_weight(tv[j].z, dv[j].z) + resid_weight(tv[j].w, dv[j].w);
     }
 #pragma unroll
-    for (int j = 0; j < kResidPerThread / 4; ++j) {
-      sr += resid_weight(tv[j].x, dv[j].x) + resid_weight(tv[j].y, dv[j].y) +
-            resid_weight(tv[j].z, dv[j].z) + resid_weight(tv[j].w, dv[j].w);
+    for (int j = 0; j < kResidPerThread / 4; ++j)
       st += target_weight(tv[j].x) + target_weight(tv[j].y) + target_weight(tv[j].z) +
             target_weight(tv[j].w);
-    }
   } else {
     for (int k = k0 + threadIdx.x; k < k1; k += kAcceptThreads) {
-      const float t = pt[row + k];
-      sr += resid_weight(t, pd[row + k]);
+      const float t = pt_row[k];
+      if (pd_row != nullptr) sr += resid_weight(t, pd_row[k]);
       st += target_weight(t);
     }
   }
-  sr = block_sum_u64(sr);
-  st = block_sum_u64(st);
-  if (threadIdx.x == 0) {
-    part[(static_cast<long>(b) * chunks + chunk) * 2 + 0] = sr;
-    part[(static_cast<long>(b) * chunks + chunk) * 2 + 1] = st;
-  }
 }
 
-__global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
-    const float* __restrict__ pt, const float* __restrict__ pd, const float* __restrict__ u_res,
-    const int32_t* __restrict__ cu_nodes, int vocab, int chunks, const int32_t* __restrict__ ws_c,
-    const uint64_t* __restrict__ part, int32_t* __restrict__ resample_token,
-    int32_t* __restrict__ err) {
+// The workgroup that takes a sequence's last ticket: total mass, exact threshold,
+// the chunk where the running sum passes it, then the element inside that chunk.
+__device__ void select_token(const AcceptArgs& a, int b, int chunks, const float* __restrict__ pt_row,
+                             const float* __restrict__ pd_row, float u) {
   __shared__ int s_mode, s_chunk;
   __shared__ uint64_t s_rem;
   __shared__ uint64_t s_part[2 * kMaxResidChunks];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  // the rejection node, the sequence's first node and the per-chunk sums (which do
-  // not depend on the node) are requested together; then the node's uniform
-  const uint64_t* mine = part + static_cast<long>(b) * chunks * 2;
-  const int c = ws_c[b];
-  const int n0 = cu_nodes[b];
-  uint64_t pv[2 * kMaxResidChunks / kAcceptThreads + 1];
-  int np = 0;
-  for (int k = tid; k < 2 * chunks; k += kAcceptThreads) pv[np++] = mine[k];
-  if (c < 0) return;
-  const float u = u_res[n0 + c];
-  np = 0;
-  for (int k = tid; k < 2 * chunks; k += kAcceptThreads) s_part[k] = pv[np++];
+  const int tid = threadIdx.x;
+  uint64_t* mine = a.part + static_cast<long>(b) * chunks * 2;
+  for (int k = tid; k < 2 * chunks; k += kAcceptThreads)
+    s_part[k] = __hip_atomic_load(mine + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (tid == 0) {
     uint64_t zr = 0, zt = 0;
@@ -367,24 +259,22 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
       s_chunk = kc;
       s_rem = t - cum;
     } else {
-      resample_token[b] = -1;
-      atomicOr(err, TV_ERR_ZERO_MASS);
+      a.resample_token[b] = -1;
+      atomicOr(a.err, TV_ERR_ZERO_MASS);
     }
   }
   __syncthreads();
   const int mode = s_mode;
   if (mode < 0) return;
-  const long row = static_cast<long>(n0 + c) * vocab;
   const int k0 = s_chunk * kResidChunk + tid * kResidPerThread;
-  const int k1 = min(vocab, min(k0 + kResidPerThread, (s_chunk + 1) * kResidChunk));
+  const int k1 = min(a.vocab, min(k0 + kResidPerThread, (s_chunk + 1) * kResidChunk));
   // this thread's weights, loaded once (all loads in flight together) and kept for
   // the walk
   uint64_t wgt[kResidPerThread];
 #pragma unroll
   for (int e = 0; e < kResidPerThread; ++e) {
     const int k = k0 + e;
-    wgt[e] = 0;
-    if (k < k1) wgt[e] = mode == 0 ? resid_weight(pt[row + k], pd[row + k]) : target_weight(pt[row + k]);
+    wgt[e] = k < k1 ? weight_at(pt_row, pd_row, k, mode) : 0ull;
   }
   uint64_t local = 0;
 #pragma unroll
@@ -400,12 +290,191 @@ __global__ void __launch_bounds__(kAcceptThreads) k_resid_select(
       run += wgt[e];
       if (tok < 0 && run > rem) tok = k0 + e;
     }
-    resample_token[b] = tok;
+    a.resample_token[b] = tok;
   }
 }
 
+// Grid (chunks, batch).  kChunked false: one chunk, the workgroup samples its row
+// alone.  Workgroup (0, b) writes the walk's outputs; with chunks, every workgroup of
+// the sequence repeats the walk (same inputs, same decisions).
+template <bool kChunked>
+__global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int batch, int chunks) {
+  __shared__ int16_t s_par[TV_MAX_NODES];
+  __shared__ uint8_t s_acc[TV_MAX_NODES];
+  __shared__ int s_bad, s_key, s_child, s_err, s_last;
+  const int tid = threadIdx.x;
+  // workgroup i runs on die i % 8: the chunks of sequence b all go to die b % 8, so
+  // the walk's gathers and the chunk the last one re-reads are shared in its L2
+  const int lin = blockIdx.x, die = lin % 8, q = lin / 8;
+  const int chunk = q % chunks, b = (q / chunks) * 8 + die;
+  if (b >= batch) return;
+  const bool writer = chunk == 0;
+  const int n0 = a.cu_nodes[b];
+  const int n = a.cu_nodes[b + 1] - n0;
+  if (tid == 0) {
+    s_bad = 0;
+    s_key = -1;
+    s_child = INT_MAX;
+    s_err = 0;
+  }
+  if (writer)
+    for (int j = tid; j < a.max_path; j += kAcceptThreads)
+      a.path[static_cast<long>(b) * a.max_path + j] = -1;
+  __syncthreads();
+  if (n > a.max_nodes) {
+    if (!writer) return;
+    if (a.node_ok != nullptr)
+      for (int i = tid; i < n; i += kAcceptThreads) a.node_ok[n0 + i] = 0;
+    if (tid == 0) {
+      atomicOr(a.err, TV_ERR_TOO_MANY_NODES);
+      a.accept_len[b] = 0;
+      a.resample_node[b] = -1;
+      a.resample_token[b] = -1;
+    }
+    return;
+  }
+  for (int i = tid; i < n; i += kAcceptThreads) {
+    const int p = a.parent[n0 + i];
+    s_par[i] = static_cast<int16_t>(p);
+    if (p >= i || p < -1) s_bad = 1;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (!writer) return;
+    if (a.node_ok != nullptr)
+      for (int i = tid; i < n; i += kAcceptThreads) a.node_ok[n0 + i] = 0;
+    if (tid == 0) {
+      atomicOr(a.err, TV_ERR_BAD_PARENT);
+      a.accept_len[b] = 0;
+      a.resample_node[b] = -1;
+      a.resample_token[b] = -1;
+    }
+    return;
+  }
+  // 1-2. ratio test per node: u < min(1, pt/pd)  <=>  (double)u * pd < pt for u in [0, 1)
+  int my_err = 0;
+  for (int i = tid; i < n; i += kAcceptThreads) {
+    const long g = n0 + i;
+    const int tok = a.token[g];
+    bool acc = false;
+    if (tok < 0 || tok >= a.vocab) {
+      my_err |= TV_ERR_TOKEN;
+    } else {
+      const float u = a.u_acc[g];
+      if (!(u >= 0.0f && u < 1.0f)) {
+        my_err |= TV_ERR_UNIFORM;
+      } else {
+        const long off = g * a.vocab + tok;
+        acc = static_cast<double>(u) * static_cast<double>(a.pd[off]) <
+              static_cast<double>(a.pt[off]);
+      }
+    }
+    s_acc[i] = acc ? 1 : 0;
+  }
+  if (my_err) atomicOr(&s_err, my_err);
+  __syncthreads();
+  // 3. a node is reached by the walk iff it and all its ancestors passed;
+  //    the winner is the reached node of largest depth, smallest index on ties
+  for (int i = tid; i < n; i += kAcceptThreads) {
+    int v = i, depth = 0;
+    bool ok = true;
+    while (v >= 0) {
+      if (!s_acc[v]) {
+        ok = false;
+        break;
+      }
+      ++depth;
+      v = s_par[v];
+    }
+    if (writer && a.node_ok != nullptr) a.node_ok[n0 + i] = ok ? 1 : 0;
+    if (ok) atomicMax(&s_key, (depth << 12) | (4095 - i));
+  }
+  __syncthreads();
+  const int key = s_key;
+  const int w = key < 0 ? -1 : 4095 - (key & 4095);
+  const int depth_w = key < 0 ? 0 : (key >> 12);
+  // rejection point: smallest-index child of the winner (w = -1: of the prefix)
+  for (int i = tid; i < n; i += kAcceptThreads)
+    if (s_par[i] == w) atomicMin(&s_child, i);
+  __syncthreads();
+  // the row to sample: the rejection node's (residual), or the bonus row at the
+  // winner's own context when the winner is a leaf
+  const int c = s_child == INT_MAX ? -1 : s_child;
+  int e = 0, snode = -1;
+  const float* row_t = nullptr;
+  const float* row_d = nullptr;
+  float u = 0.0f;
+  if (c >= 0) {
+    snode = c;
+    u = a.u_res[n0 + c];
+    if (u >= 0.0f && u < 1.0f) {
+      row_t = a.pt + static_cast<long>(n0 + c) * a.vocab;
+      row_d = a.pd + static_cast<long>(n0 + c) * a.vocab;
+    } else {
+      e |= TV_ERR_UNIFORM;
+    }
+  } else if (w >= 0 && a.own_row != nullptr) {
+    const int r = a.own_row[n0 + w];
+    if (r < -1 || r >= a.own_rows) {
+      e |= TV_ERR_ROW;
+    } else if (r >= 0) {
+      snode = w;
+      u = a.u_res[n0 + w];
+      if (u >= 0.0f && u < 1.0f) row_t = a.p_own + static_cast<long>(r) * a.vocab;
+      else e |= TV_ERR_UNIFORM;
+    }
+  }
+  if (writer && tid == 0) {
+    e |= s_err;
+    a.accept_len[b] = depth_w;
+    int v = w;
+    for (int k = depth_w - 1; k >= 0; --k) {
+      if (k < a.max_path) a.path[static_cast<long>(b) * a.max_path + k] = v;
+      v = s_par[v];
+    }
+    if (depth_w > a.max_path) e |= TV_ERR_PATH;
+    a.resample_node[b] = snode;
+    if (row_t == nullptr) a.resample_token[b] = -1;
+    if (e) atomicOr(a.err, e);
+  }
+  if (row_t == nullptr) return;
+  if constexpr (!kChunked) {
+    sample_in_block(row_t, row_d, a.vocab, u, a.resample_token + b, a.err);
+  } else {
+    uint64_t sr, st;
+    chunk_sums(row_t, row_d, a.vocab, chunk, sr, st);
+    sr = block_sum_u64(sr);
+    st = block_sum_u64(st);
+    // publish the chunk's sums and take a ticket; the last of the sequence's
+    // workgroups selects.  The sums are written by device-scope atomic exchanges,
+    // which complete at the device's coherence point before they return (the wait
+    // below), and only then is the ticket taken; the selecting workgroup reads them
+    // with device-scope atomic loads.  So it sees every chunk's sums whichever die
+    // wrote them, without a cache-wide release or acquire (an L2 write-back per
+    // workgroup made 64 sequences x 32 chunks take 63 us instead of 28).
+    if (tid == 0) {
+      uint64_t* slot = a.part + (static_cast<long>(b) * chunks + chunk) * 2;
+      const uint64_t o0 = __hip_atomic_exchange(slot, sr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t o1 =
+          __hip_atomic_exchange(slot + 1, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" : : "v"(o0), "v"(o1) : "memory");  // both returned
+      const bool last = __hip_atomic_fetch_add(a.tickets + b, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) == chunks - 1;
+      // every workgroup of the sequence has taken its ticket: zero it for the next call
+      if (last) __hip_atomic_store(a.tickets + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    select_token(a, b, chunks, row_t, row_d, u);
+  }
+}
+
+}  // namespace
+
 }  // namespace tv
 
+// Workspace: [batch] finish tickets (256-byte aligned), then [batch, chunks, 2] sums.
 extern "C" size_t tree_accept_workspace_size(int32_t batch, int32_t vocab) {
   if (batch <= 0 || vocab <= 0) return 0;
   const size_t chunks = static_cast<size_t>(tv::ceil_div(vocab, tv::kResidChunk));
@@ -413,53 +482,88 @@ extern "C" size_t tree_accept_workspace_size(int32_t batch, int32_t vocab) {
   return head + static_cast<size_t>(batch) * chunks * 2 * sizeof(uint64_t);
 }
 
+namespace tv {
+
+// Shared body of tree_accept and its variants: checks, then one launch.
+int accept_launch(const char* fn, const float* p_target, const float* p_draft,
+                  const int32_t* token, const float* u_accept, const float* u_resample,
+                  const int32_t* parent, const int32_t* cu_nodes, const float* p_own,
+                  const int32_t* own_row, int32_t own_rows, int32_t batch, int32_t total_nodes,
+                  int32_t max_nodes, int32_t vocab, int32_t max_path, int32_t* accept_len,
+                  int32_t* path, int32_t* resample_node, int32_t* resample_token,
+                  uint8_t* node_ok, void* workspace, size_t workspace_bytes, int32_t* err,
+                  void* stream) {
+  char msg[160];
+  auto bad = [&](int status, const char* what) {
+    snprintf(msg, sizeof(msg), "%s: %s", fn, what);
+    return fail(status, msg);
+  };
+  if (batch < 0 || total_nodes < 0 || max_path < 0 || own_rows < 0)
+    return bad(TV_EINVAL, "negative size");
+  if (vocab <= 0 || vocab > kMaxVocab)
+    return bad(TV_EUNSUPPORTED, "vocab must be in [1, 262144]");
+  if (max_nodes < 1 || max_nodes > TV_MAX_NODES)
+    return bad(TV_EUNSUPPORTED, "max_nodes must be in [1, 2048]");
+  if (batch == 0) return TV_OK;
+  if (cu_nodes == nullptr || err == nullptr || accept_len == nullptr ||
+      resample_node == nullptr || resample_token == nullptr || (max_path > 0 && path == nullptr))
+    return bad(TV_EINVAL, "null output or cu_nodes/err");
+  if (total_nodes > 0 && (p_target == nullptr || p_draft == nullptr || token == nullptr ||
+                          u_accept == nullptr || u_resample == nullptr || parent == nullptr))
+    return bad(TV_EINVAL, "null input array");
+  if (own_row != nullptr && own_rows > 0 && p_own == nullptr)
+    return bad(TV_EINVAL, "own_row given without p_own");
+  const int chunks = ceil_div(vocab, kResidChunk);
+  const bool chunked = vocab > kFusedVocab;
+  if (chunked && (workspace == nullptr || workspace_bytes < tree_accept_workspace_size(batch, vocab)))
+    return bad(TV_EWORKSPACE, "workspace missing or too small");
+  AcceptArgs a{};
+  a.pt = p_target;
+  a.pd = p_draft;
+  a.token = token;
+  a.u_acc = u_accept;
+  a.u_res = u_resample;
+  a.parent = parent;
+  a.cu_nodes = cu_nodes;
+  a.p_own = p_own;
+  a.own_row = own_row;
+  a.own_rows = own_row != nullptr ? own_rows : 0;
+  a.max_nodes = max_nodes;
+  a.vocab = vocab;
+  a.max_path = max_path;
+  a.accept_len = accept_len;
+  a.path = path;
+  a.resample_node = resample_node;
+  a.resample_token = resample_token;
+  a.node_ok = node_ok;
+  a.err = err;
+  auto s = static_cast<hipStream_t>(stream);
+  const int padded = ceil_div(batch, 8) * 8;
+  if (!chunked) {
+    hipLaunchKernelGGL(k_accept<false>, dim3(padded), dim3(kAcceptThreads), 0, s, a, batch, 1);
+  } else {
+    const size_t head = (static_cast<size_t>(batch) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+    a.tickets = static_cast<int*>(workspace);
+    a.part = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + head);
+    hipLaunchKernelGGL(k_accept<true>, dim3(padded * chunks), dim3(kAcceptThreads), 0, s, a,
+                       batch, chunks);
+  }
+  return check_launch(fn);
+}
+
+}  // namespace tv
+
 extern "C" int tree_accept(const float* p_target, const float* p_draft, const int32_t* token,
                            const float* u_accept, const float* u_resample, const int32_t* parent,
-                           const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
+                           const int32_t* cu_nodes, const float* p_own, const int32_t* own_row,
+                           int32_t own_rows, int32_t batch, int32_t total_nodes,
                            int32_t max_nodes, int32_t vocab, int32_t max_path,
                            int32_t* accept_len, int32_t* path, int32_t* resample_node,
                            int32_t* resample_token, uint8_t* node_ok, void* workspace,
                            size_t workspace_bytes, int32_t* err, void* stream) {
   tv::clear_error();
-  if (batch < 0 || total_nodes < 0 || max_path < 0)
-    return tv::fail(TV_EINVAL, "tree_accept: negative size");
-  if (vocab <= 0 || vocab > tv::kMaxVocab)
-    return tv::fail(TV_EUNSUPPORTED, "tree_accept: vocab must be in [1, 262144]");
-  if (max_nodes < 1 || max_nodes > TV_MAX_NODES)
-    return tv::fail(TV_EUNSUPPORTED, "tree_accept: max_nodes must be in [1, 2048]");
-  if (batch == 0) return TV_OK;
-  if (cu_nodes == nullptr || err == nullptr || accept_len == nullptr ||
-      resample_node == nullptr || resample_token == nullptr || (max_path > 0 && path == nullptr))
-    return tv::fail(TV_EINVAL, "tree_accept: null output or cu_nodes/err");
-  if (total_nodes > 0 && (p_target == nullptr || p_draft == nullptr || token == nullptr ||
-                          u_accept == nullptr || u_resample == nullptr || parent == nullptr))
-    return tv::fail(TV_EINVAL, "tree_accept: null input array");
-  const size_t need = tree_accept_workspace_size(batch, vocab);
-  if (workspace == nullptr || workspace_bytes < need)
-    return tv::fail(TV_EWORKSPACE, "tree_accept: workspace missing or too small");
-  auto s = static_cast<hipStream_t>(stream);
-  const int chunks = tv::ceil_div(vocab, tv::kResidChunk);
-  int32_t* ws_c = static_cast<int32_t*>(workspace);
-  const size_t head = (static_cast<size_t>(batch) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
-  uint64_t* part = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + head);
-  if (vocab <= tv::kFusedVocab) {  // one kernel: the walk's workgroup also resamples
-    hipLaunchKernelGGL(tv::k_accept_walk<true>, dim3(batch), dim3(tv::kAcceptThreads), 0, s,
-                       p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes,
-                       vocab, max_path, accept_len, path, resample_node, resample_token, node_ok,
-                       ws_c, err);
-    return tv::check_launch("tree_accept/walk");
-  }
-  hipLaunchKernelGGL(tv::k_accept_walk<false>, dim3(batch), dim3(tv::kAcceptThreads), 0, s,
-                     p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes, max_nodes,
-                     vocab, max_path, accept_len, path, resample_node, resample_token, node_ok,
-                     ws_c, err);
-  int st = tv::check_launch("tree_accept/walk");
-  if (st != TV_OK) return st;
-  hipLaunchKernelGGL(tv::k_resid_partial, dim3(chunks, batch), dim3(tv::kAcceptThreads), 0, s,
-                     p_target, p_draft, cu_nodes, vocab, chunks, ws_c, part);
-  st = tv::check_launch("tree_accept/partial");
-  if (st != TV_OK) return st;
-  hipLaunchKernelGGL(tv::k_resid_select, dim3(batch), dim3(tv::kAcceptThreads), 0, s, p_target,
-                     p_draft, u_resample, cu_nodes, vocab, chunks, ws_c, part, resample_token, err);
-  return tv::check_launch("tree_accept/select");
+  return tv::accept_launch("tree_accept", p_target, p_draft, token, u_accept, u_resample, parent,
+                           cu_nodes, p_own, own_row, own_rows, batch, total_nodes, max_nodes,
+                           vocab, max_path, accept_len, path, resample_node, resample_token,
+                           node_ok, workspace, workspace_bytes, err, stream);
 }

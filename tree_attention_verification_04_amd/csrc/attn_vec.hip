@@ -3,7 +3,8 @@
 // This is the precise path (fp32 end to end, natural exp) used for fp32 inputs
 // and for head sizes the matrix-core kernel does not take; it also serves as an
 // independent cross-check of that kernel.  One wavefront per (node, query head)
-// row.  Keys are taken 64 at a time, one key per lane: first the prefix, one
+// row.  Keys are taken 64 at a time, one key per lane for the scores and one key
+// row per step, read by the whole wavefront, for P.V: first the prefix, one
 // paged block per step, then each 64-node word of the row's ancestor bitset
 // (page "端云协同推测解码中草稿模型动态生成与验证并行化：探究树形注意力机制与显存碎片整理联合加速"
 // (ufo.work/2026/537), §2.2.2 mask M_tree, appendix B ancestor bitmap and online
@@ -104,8 +105,10 @@ __global__ void __launch_bounds__(256) k_attn_vec(AttnArgs a) {
   const uint64_t* anc_row = a.anc + static_cast<long>(node) * a.words;
   for (int c = 0; c < nblk + ntw; ++c) {
     bool valid;
-    const T* krow = nullptr;
-    const T* vrow = nullptr;
+    const T* kbase = nullptr;  // key 0 of the tile; key k at kbase + k * stride
+    const T* vbase = nullptr;
+    long stride;
+    int nrows;                 // rows of the tile that exist in memory
     if (c < nblk) {
       const int t = c * 64 + lane;
       int blk = a.block_table[static_cast<long>(b) * a.max_blocks + c];
@@ -114,19 +117,24 @@ __global__ void __launch_bounds__(256) k_attn_vec(AttnArgs a) {
         continue;
       }
       valid = t < plen;
-      const long base = ((static_cast<long>(blk) * a.hkv + g) * 64 + lane) * D;
-      krow = kc + base;
-      vrow = vc + base;
+      const long base = (static_cast<long>(blk) * a.hkv + g) * 64 * D;
+      kbase = kc + base;
+      vbase = vc + base;
+      stride = D;
+      nrows = 64;  // a paged block always holds 64 rows
     } else {
       const int w = c - nblk;
       const uint64_t word = anc_row[w];
       if (word == 0) continue;
       valid = ((word >> lane) & 1ull) && w * 64 + lane < count;
-      const long base = (static_cast<long>(n0 + w * 64 + lane) * a.hkv + g) * D;
-      krow = kt + base;  // only dereferenced when valid (node index < count)
-      vrow = vt + base;
+      const long base = (static_cast<long>(n0 + w * 64) * a.hkv + g) * D;
+      kbase = kt + base;
+      vbase = vt + base;
+      stride = static_cast<long>(a.hkv) * D;
+      nrows = min(64, count - w * 64);
     }
-    const float s = valid ? dot_row<T, D>(krow, qs) * a.scale : -INFINITY;
+    const float s =
+        valid ? dot_row<T, D>(kbase + static_cast<long>(lane) * stride, qs) * a.scale : -INFINITY;
     const float m_new = fmaxf(m, wave_max(s));
     if (m_new == -INFINITY) continue;
     const float p = valid ? expf(s - m_new) : 0.0f;
@@ -134,15 +142,21 @@ __global__ void __launch_bounds__(256) k_attn_vec(AttnArgs a) {
     l = l * alpha + wave_sum(p);
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] *= alpha;
-    const uintptr_t vaddr = reinterpret_cast<uintptr_t>(vrow);
+    // P.V: lane owns output dims lane + 64 j; key k's row is read by the whole wave
+    // (coalesced); every row's loads are issued before the first is used, rows past
+    // the tile's end repeat its last row with probability 0
+    float vv[64][PER];
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      const T* vk = vbase + static_cast<long>(min(k, nrows - 1)) * stride;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) vv[k][j] = load_elem(vk, lane + 64 * j);
+    }
+#pragma unroll
     for (int k = 0; k < 64; ++k) {
       const float pk = __shfl(p, k, 64);
-      if (pk == 0.0f) continue;
-      const uint32_t lo = __shfl(static_cast<uint32_t>(vaddr), k, 64);
-      const uint32_t hi = __shfl(static_cast<uint32_t>(vaddr >> 32), k, 64);
-      const T* vk = reinterpret_cast<const T*>((static_cast<uintptr_t>(hi) << 32) | lo);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) acc[j] = fmaf(pk, load_elem(vk, lane + 64 * j), acc[j]);
+      for (int j = 0; j < PER; ++j) acc[j] = fmaf(pk, vv[k][j], acc[j]);
     }
     m = m_new;
   }
