@@ -26,7 +26,8 @@
  *   - Every array pointer is DEVICE memory owned by the caller; the library
  *     keeps no pointer after a call returns.  The library allocates nothing:
  *     scratch comes from a caller-provided workspace whose size is returned
- *     by the matching *_workspace_size query.
+ *     by the matching *_workspace_size query (tree_accept_noalloc instead uses
+ *     a fixed scratch array of the library, one per GPU).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued on it; no call synchronises the device or the host.
  *     Buffers must stay alive until the stream has passed the call.
@@ -278,6 +279,29 @@ int tree_accept(const float* p_target, const float* p_draft, const int32_t* toke
                 int32_t vocab, int32_t max_path, int32_t* accept_len, int32_t* path,
                 int32_t* resample_node, int32_t* resample_token, uint8_t* node_ok,
                 void* workspace, size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * tree_accept_noalloc — tree_accept for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, outputs, launch and errors as tree_accept, minus
+ * the workspace: the chunked launch (vocab > 65536) keeps its ticket words and
+ * chunk sums in a fixed scratch array of this library, one copy per GPU (1 MiB +
+ * 4 KiB, held until the process ends; its device address is looked up once per
+ * device and its ticket words cleared then).  Nothing is allocated per call.
+ *
+ *   limits       vocab > 65536 needs batch <= 1024 (else TV_EUNSUPPORTED, nothing
+ *                launched); smaller vocabularies use no scratch and have no limit
+ *   concurrency  every call on one GPU shares that GPU's scratch: calls that can
+ *                overlap on the device (different streams, or graphs replayed
+ *                concurrently) race and must be serialised by the caller
+ */
+int tree_accept_noalloc(const float* p_target, const float* p_draft, const int32_t* token,
+                        const float* u_accept, const float* u_resample, const int32_t* parent,
+                        const int32_t* cu_nodes, const float* p_own, const int32_t* own_row,
+                        int32_t own_rows, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                        int32_t vocab, int32_t max_path, int32_t* accept_len, int32_t* path,
+                        int32_t* resample_node, int32_t* resample_token, uint8_t* node_ok,
+                        int32_t* err, void* stream);
 
 /*
  * tree_commit_kv — append each sequence's accepted path to its paged prefix.

@@ -44,6 +44,7 @@ EXPORTS = (
     "tree_draft_build",
     "tree_accept_workspace_size",
     "tree_accept",
+    "tree_accept_noalloc",
     "tree_commit_kv",
     "tree_softmax_rows_workspace_size",
     "tree_softmax_rows",
@@ -80,6 +81,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_accept.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
                                 Z, P, P]
     lib.tree_accept.restype = ctypes.c_int
+    lib.tree_accept_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P,
+                                        P, P]
+    lib.tree_accept_noalloc.restype = ctypes.c_int
     lib.tree_commit_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, I, P, I, P, P, P]
     lib.tree_commit_kv.restype = ctypes.c_int
     lib.tree_softmax_rows_workspace_size.argtypes = [I, I]
@@ -393,6 +397,48 @@ def tree_accept(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes
                            _ptr(o["resample_node"]), _ptr(o["resample_token"]),
                            _ptr(o.get("node_ok")), _ptr(workspace),
                            workspace.numel(), _ptr(err), _stream(stream)))
+    return o
+
+
+def tree_accept_noalloc(p_target, p_draft, token, u_accept, u_resample, parent, cu_nodes,
+                        max_nodes: int, max_path: int, *, p_own=None, own_row=None, outputs: dict,
+                        err: torch.Tensor, stream=None) -> dict:
+    """tree_accept without a workspace: the chunked launch uses the library's fixed
+    per-GPU scratch (at most 1024 sequences above 65536 vocabulary entries).  The
+    caller passes every output (outputs: accept_len, path, resample_node,
+    resample_token, node_ok or None) and the error word; nothing is allocated here.
+    Calls that overlap on one GPU race on the scratch."""
+    lib = load()
+    _need(p_target, "p_target", torch.float32, 2)
+    _need(p_draft, "p_draft", torch.float32, 2)
+    for name, t in (("token", token), ("parent", parent), ("cu_nodes", cu_nodes)):
+        _need(t, name, torch.int32, 1)
+    for name, t in (("u_accept", u_accept), ("u_resample", u_resample)):
+        _need(t, name, torch.float32, 1)
+    total, vocab = p_target.shape
+    if tuple(p_draft.shape) != (total, vocab):
+        raise ValueError("p_draft must match p_target")
+    if (p_own is None) != (own_row is None):
+        raise ValueError("p_own and own_row go together")
+    own_rows = 0
+    if p_own is not None:
+        _need(p_own, "p_own", torch.float32, 2)
+        _need(own_row, "own_row", torch.int32, 1)
+        if p_own.shape[1] != vocab or own_row.numel() != total:
+            raise ValueError("p_own must be [rows, vocab] and own_row [total_nodes]")
+        own_rows = p_own.shape[0]
+    batch = cu_nodes.numel() - 1
+    _need(err, "err", torch.int32)
+    o = outputs
+    if tuple(o["path"].shape) != (batch, max_path):
+        raise ValueError("outputs['path'] must be [batch, max_path]")
+    _check("tree_accept_noalloc",
+           lib.tree_accept_noalloc(_ptr(p_target), _ptr(p_draft), _ptr(token), _ptr(u_accept),
+                                   _ptr(u_resample), _ptr(parent), _ptr(cu_nodes), _ptr(p_own),
+                                   _ptr(own_row), own_rows, batch, total, max_nodes, vocab,
+                                   max_path, _ptr(o["accept_len"]), _ptr(o["path"]),
+                                   _ptr(o["resample_node"]), _ptr(o["resample_token"]),
+                                   _ptr(o.get("node_ok")), _ptr(err), _stream(stream)))
     return o
 
 
