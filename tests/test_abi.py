@@ -135,15 +135,18 @@ def test_fp8_attention_host_checks(lib):
     assert fp8_call(lib, max_prefix=200) == tv.TV_EINVAL
     assert b"tree_verify_attention_fp8kv" in lib.tree_last_error()
     assert fp8_call(lib, batch=0) == tv.TV_OK                  # nothing to do
-    # the FP8 cache runs the register-staged kernel: split partials, never a pair order
+    # the FP8 cache is laid out like the bf16 one (its long items run the pipelined
+    # kernel's register path): split partials of a short verify
     rows = 64 * 32
     need = lib.tree_verify_attention_fp8kv_workspace_size(1, 64, 64, 1088, 32, 32)
     # 2048 bytes of counter words first (every attention workspace keeps them), then
     # 5 splits of 4 blocks
     assert need == 2048 + 5 * rows * 128 * 4 + 5 * rows * 4
-    # 640 work items (80 per die) run persistently: the counter words (queue heads) only
-    assert lib.tree_verify_attention_fp8kv_workspace_size(8, 4672, 584, 4096, 32, 8) == 2048
-    # 256 items (32 per die) fill one round: no workspace
+    # the same plans as bf16: persistent with cut tail items (wide tree), one round
+    # (long context: no workspace)
+    for shape in ((8, 4672, 584, 4096, 32, 8), (4, 1024, 256, 32768, 64, 8), (1, 64, 64, 1088, 32, 32)):
+        assert lib.tree_verify_attention_fp8kv_workspace_size(*shape) == \
+            lib.tree_verify_attention_workspace_size(*shape, 128, tv.TV_DTYPE_BF16)
     assert lib.tree_verify_attention_fp8kv_workspace_size(4, 1024, 256, 32768, 64, 8) == 0
     assert fp8_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
                     ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE

@@ -92,14 +92,36 @@ def test_fp8_attention_small(gpu_lib, name, mode):
     check_fp8(gpu_lib, case, mode, seed=31)
 
 
-@pytest.mark.parametrize("index", [1, 2, 3])
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
 def test_fp8_attention_full_configs(gpu_lib, index):
-    """The LLaVA-like, wide-tree and serving workloads with quantized caches, sampled
-    nodes."""
+    """The four bf16 workloads with quantized caches, in the benchmark's launch
+    configuration: first, last and random nodes of every sequence."""
     case = W.make_config(index, with_probs=False)
-    seqs = None if case.batch <= 8 else {0, 7, 31, 63}
     check_fp8(gpu_lib, case, "quant", seed=index,
-              nodes=sample_nodes(case, 12, seed=index, seqs=seqs))
+              nodes=sample_nodes(case, 12 if case.batch <= 8 else 2, seed=index))
+
+
+# Long work items of the pipelined kernel's FP8 register path: cut tail items merged
+# by tickets (64 pairs x 10 row tiles), sequences without prefix or with a single
+# node, prefixes that end inside a block; tree tiles staged through the same registers.
+FP8_TAIL = ([W.tree_kary_levels(8, 3)] * 5 + [W.tree_random(np.random.default_rng(12), 300, 8),
+             W.tree_chain(1), np.zeros(0, np.int32)], [300, 0, 4096, 64, 65, 1000, 130, 5], 32, 8)
+
+
+@pytest.mark.parametrize("mode", ["codes", "quant"])
+def test_fp8_attention_tail_pieces(gpu_lib, mode):
+    parents, plens, hq, hkv = FP8_TAIL
+    case = W.make_case("fp8tail", parents, plens, hq, hkv, 128, W.DT_BF16, 10, 27, with_probs=False)
+    check_fp8(gpu_lib, case, mode, seed=8, nodes=sample_nodes(case, 8, seed=2))
+
+
+def test_fp8_attention_repeatable(gpu_lib):
+    """Persistent FP8 launches give the same bits call after call."""
+    case = W.make_config(3, with_probs=False)
+    k8, v8, ks, vs = fp8_inputs(case, "quant", 3)
+    first, first_lse, _ = run_fp8(gpu_lib, case, k8, v8, ks, vs)
+    again, again_lse, err = run_fp8(gpu_lib, case, k8, v8, ks, vs)
+    assert err == 0 and torch.equal(first, again) and torch.equal(first_lse, again_lse)
 
 
 def test_fp8_bad_block_sets_error(gpu_lib):

@@ -45,8 +45,9 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
     p.splits = 1;
   }
   p.total_work = base * p.splits;
-  // an FP8 prefix cache is dequantized by the register-staged kernel, whatever the length
-  p.long_items = !fp8_kv && p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
+  // (an FP8 prefix cache goes through the pipelined kernel's register path for long
+  // items, through the register-staged kernel for short ones)
+  p.long_items = p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
   // more long work items than compute units, from sequences of different lengths:
   // rank the (sequence, KV head) pairs by cost and start the longest first
   const long pairs = static_cast<long>(batch) * hkv;

@@ -95,6 +95,21 @@ __device__ __forceinline__ void issue_loads(const void* kb, uint32_t ko0, uint32
       : "memory");
 }
 
+// The ancestor dword of this lane's row alone (the FP8 pipeline's one direct load per
+// iteration; its tiles come through registers).
+__device__ __forceinline__ void issue_anc_load(const void* ab, uint32_t ao, uint32_t lds_a) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[la]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %[a0], %[ab]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [a0] "v"(ao), [ab] "s"(ab), [la] "s"(lds_a)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier; the empty asm statements keep the
 // compiler from moving LDS accesses across the barrier
 template <int N>
@@ -117,7 +132,14 @@ struct Slot {
 
 }  // namespace
 
-// One work item: slot k_slot of die xcd's list.
+// One work item: slot k_slot of die xcd's list.  kFp8: the paged prefix cache holds
+// E4M3 bytes with a scale per (block, KV head, position); every tile then reaches LDS
+// through registers, two tiles ahead of its use: the registers of tile t are loaded in
+// iteration t - 4 and written to the bf16 rings in iteration t - 2 (an FP8 prefix tile
+// dequantized on the way, byte x scale rounded to bf16; a tree tile copied), so the
+// rest of the kernel is the bf16 one.  Each iteration still issues five loads per lane
+// (four register loads and the ancestor dword), so the same wait holds.
+template <bool kFp8>
 __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, const int k_slot) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kMaskOff);
@@ -283,6 +305,71 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
                 lds_kv + kVOff + slot_v * kTileBytes);
   };
 
+  // ---- FP8 pipeline: a tile's registers.  FP8 prefix tile: thread t holds the 16
+  // E4M3 bytes 16 (t % 8) .. of key t / 8 of K (a) and V (b) and that key's scales
+  // (c.x, d.x); bf16 tree tile: chunks t and t + 512 of K (a, b) and V (c, d).
+  struct Regs {
+    uint4 a, b, c, d;
+  };
+  const uint8_t* k8 = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* v8 = static_cast<const uint8_t*>(a.v_cache);
+  auto load_regs = [&](int it, Regs& r) __attribute__((always_inline)) {
+    int kind, base;
+    tile_kind(min(it, n_tiles - 1), kind, base);
+    if (kind == 0) {
+      int blk = bt_row[base / kKT];
+      int nvalid = min(kKT, plen - base);
+      if (blk < 0 || blk >= a.num_blocks) {
+        if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
+        blk = 0;  // block 0 stands in; the sequence is flagged
+        nvalid = 1;
+      }
+      const long row0 = (static_cast<long>(blk) * a.hkv + g) * kKT;
+      const long key = row0 + min(tid >> 3, nvalid - 1);
+      r.a = *reinterpret_cast<const uint4*>(k8 + key * kD + 16 * (tid & 7));
+      r.b = *reinterpret_cast<const uint4*>(v8 + key * kD + 16 * (tid & 7));
+      r.c.x = __float_as_uint(a.k_scale[key]);
+      r.d.x = __float_as_uint(a.v_scale[key]);
+    } else {
+      const int nvalid = min(64, count - base * 64);
+      const long row0 = static_cast<long>(n0 + base * 64);
+      const int key0 = min(tid >> 4, nvalid - 1), key1 = min((tid + kTL) >> 4, nvalid - 1);
+      const long o0 = ((row0 + key0) * a.hkv + g) * kD * 2 + 16 * (tid & 15);
+      const long o1 = ((row0 + key1) * a.hkv + g) * kD * 2 + 16 * (tid & 15);
+      r.a = *reinterpret_cast<const uint4*>(kt + o0);
+      r.b = *reinterpret_cast<const uint4*>(kt + o1);
+      r.c = *reinterpret_cast<const uint4*>(vt + o0);
+      r.d = *reinterpret_cast<const uint4*>(vt + o1);
+    }
+  };
+  auto store_regs = [&](int it, int slot, const Regs& r) __attribute__((always_inline)) {
+    int kind, base;
+    tile_kind(min(it, n_tiles - 1), kind, base);
+    char* kst = smem + slot * kTileBytes;
+    char* vst = smem + kVOff + slot * kTileBytes;
+    if (kind == 0) {
+      const int key = tid >> 3, c8 = tid & 7;
+      const float sk = __uint_as_float(r.c.x), sv = __uint_as_float(r.d.x);
+      *reinterpret_cast<uint4*>(kst + k_off(key, 2 * c8)) = fp8x8_to_bf16(r.a.x, r.a.y, sk);
+      *reinterpret_cast<uint4*>(kst + k_off(key, 2 * c8 + 1)) = fp8x8_to_bf16(r.a.z, r.a.w, sk);
+      *reinterpret_cast<uint4*>(vst + v_off(key, 2 * c8)) = fp8x8_to_bf16(r.b.x, r.b.y, sv);
+      *reinterpret_cast<uint4*>(vst + v_off(key, 2 * c8 + 1)) = fp8x8_to_bf16(r.b.z, r.b.w, sv);
+    } else {
+      const int key0 = tid >> 4, key1 = (tid + kTL) >> 4, c = tid & 15;
+      *reinterpret_cast<uint4*>(kst + k_off(key0, c)) = r.a;
+      *reinterpret_cast<uint4*>(kst + k_off(key1, c)) = r.b;
+      *reinterpret_cast<uint4*>(vst + v_off(key0, c)) = r.c;
+      *reinterpret_cast<uint4*>(vst + v_off(key1, c)) = r.d;
+    }
+  };
+  auto issue_anc = [&](int it, int slot) __attribute__((always_inline)) {
+    int kind, base;
+    tile_kind(min(it, n_tiles - 1), kind, base);
+    issue_anc_load(anc_base, kind == 0 ? anc_lane : anc_lane + base * 8,
+                   lds_anc + slot * kAncSlotBytes);
+  };
+  Regs rx{}, ry{};  // registers of even and odd tiles
+
   // The first three tiles' loads do not depend on the tree mask when they are all
   // prefix tiles: then they are issued before the mask pass, whose ancestor-word
   // loads overlap them (the tiles are older than those loads, so the compiler's
@@ -290,16 +377,30 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
   // half-step with zero probabilities, is cleared.
   Src sv{};  // V source of the next iteration's loads
   auto prologue = [&]() __attribute__((always_inline)) {
-    sv = tile_src(2);
-    const Src t0 = tile_src(0), t1 = tile_src(1);
-    issue(t0, 0, t0, 0);
-    issue(t1, 1, t0, 0);
-    issue(sv, 2, t1, 1);
+    if constexpr (kFp8) {
+      // tiles 0 and 1 into the rings now, tiles 2 and 3 into registers; the
+      // ancestor words of tiles 0, 1 and 2
+      load_regs(0, rx);
+      load_regs(1, ry);
+      store_regs(0, 0, rx);
+      store_regs(1, 1, ry);
+      issue_anc(0, 0);
+      issue_anc(1, 1);
+      issue_anc(2, 2);
+      load_regs(2, rx);
+      load_regs(3, ry);
+    } else {
+      sv = tile_src(2);
+      const Src t0 = tile_src(0), t1 = tile_src(1);
+      issue(t0, 0, t0, 0);
+      issue(t1, 1, t0, 0);
+      issue(sv, 2, t1, 1);
+    }
     uint4* vz = reinterpret_cast<uint4*>(smem + kVOff + 3 * kTileBytes);
 #pragma unroll
     for (int j = 0; j < kTileBytes / 16 / kTL; ++j) vz[tid + kTL * j] = make_uint4(0, 0, 0, 0);
   };
-  const bool early = n_prefix_tiles >= 3;
+  const bool early = n_prefix_tiles >= (kFp8 ? 4 : 3);
   if (early) prologue();
 
   // ---- which 64-node tree tiles any row of this workgroup can see
@@ -469,9 +570,18 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     // tile iteration i (ring slot S = i % 4) = half-steps 2i and 2i+1
     auto body = [&](int i, auto slot) __attribute__((always_inline)) {
       constexpr int S = decltype(slot)::value;
-      const Src sk = tile_src(i + 3);
-      issue(sk, (S + 3) % kRing, sv, (S + 2) % kRing);
-      sv = sk;
+      if constexpr (kFp8) {
+        // tile i+2 from its registers into the rings, then the ancestor word of tile
+        // i+3 and the registers of tile i+4 (the same registers, now free)
+        Regs& r = (S % 2 == 0) ? rx : ry;
+        store_regs(i + 2, (S + 2) % kRing, r);
+        issue_anc(i + 3, (S + 3) % kRing);
+        load_regs(i + 4, r);
+      } else {
+        const Src sk = tile_src(i + 3);
+        issue(sk, (S + 3) % kRing, sv, (S + 2) % kRing);
+        sv = sk;
+      }
       if (wave_live) {
         uint32_t w = ~0u;
         const bool full = tile_vis(i, S, w);
@@ -622,29 +732,36 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
 }
 
 // Work items as run_work_items hands them out (kQueued: persistent, from the queues).
-template <bool kQueued>
+template <bool kQueued, bool kFp8>
 __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   run_work_items<kQueued>(a, reinterpret_cast<int*>(smem + kMaskOff + 8),
                  [](const AttnArgs& args, int die, int k_slot) __attribute__((always_inline)) {
-                   long_item(args, die, k_slot);
+                   long_item<kFp8>(args, die, k_slot);
                  });
 }
 
 int launch_attn_long(const AttnArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_long<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_long<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
+    const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_long<false, false>),
+                          reinterpret_cast<const void*>(&k_attn_long<true, false>),
+                          reinterpret_cast<const void*>(&k_attn_long<false, true>),
+                          reinterpret_cast<const void*>(&k_attn_long<true, true>)};
+    for (const void* f : fns)
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
     attr_set = true;
   }
-  if (a.queue != nullptr)
-    hipLaunchKernelGGL(k_attn_long<true>, dim3(kCUs), dim3(kTL), kSmemL, s, a);
+  const bool fp8 = a.k_scale != nullptr, queued = a.queue != nullptr;
+  const dim3 grid(queued ? kCUs : 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits);
+  if (queued && fp8)
+    hipLaunchKernelGGL((k_attn_long<true, true>), grid, dim3(kTL), kSmemL, s, a);
+  else if (queued)
+    hipLaunchKernelGGL((k_attn_long<true, false>), grid, dim3(kTL), kSmemL, s, a);
+  else if (fp8)
+    hipLaunchKernelGGL((k_attn_long<false, true>), grid, dim3(kTL), kSmemL, s, a);
   else
-    hipLaunchKernelGGL(k_attn_long<false>, dim3(8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits),
-                       dim3(kTL), kSmemL, s, a);
+    hipLaunchKernelGGL((k_attn_long<false, false>), grid, dim3(kTL), kSmemL, s, a);
   const int st = check_launch("tree_verify_attention/long");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);
