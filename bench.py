@@ -159,6 +159,29 @@ def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> 
     print(open(traffic_path(config)).read())
 
 
+def summarize_trace(config: int, db_path: str, command: str) -> None:
+    """Kernel-trace statistics (calls, total, average and share of time per kernel)
+    from a rocprofv3 results database, written to profiles/ as markdown."""
+    import sqlite3
+    import workloads as W
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select name, count(*), sum(end - start), avg(end - start) from kernels "
+                       "group by name order by 3 desc").fetchall()
+    total = sum(r[2] for r in rows) or 1
+    name = W.CONFIG_NAMES[config]
+    out = os.path.join(ROOT, "profiles", f"verify_step_{name.split(':')[0]}_kernel_trace.md")
+    with open(out, "w") as fh:
+        fh.write(f"# Verify step, workload {config} ({name}): kernel trace\n\n")
+        fh.write("Command (run from the repository root on one MI355X):\n\n```\n" + command + "\n```\n\n")
+        fh.write("Durations in microseconds from the run's results database; the bench times "
+                 "the step, the attention call and the acceptance call alone, and beside them the "
+                 "FP8-cache variant, draft-tree construction, probability rows and KV commit.\n\n")
+        fh.write("| kernel | calls | total us | average us | % |\n|---|---|---|---|---|\n")
+        for n, c, tot, avg in rows:
+            fh.write(f"| {n[:140]} | {c} | {tot / 1e3:.1f} | {avg / 1e3:.3f} | {100.0 * tot / total:.1f} |\n")
+    print(open(out).read())
+
+
 def measure_commit(tv, case, dev, acc_out, max_path: int, reps: int) -> dict:
     """tree_commit_kv after this step's acceptance, timed alone (not part of the step).
 
@@ -603,9 +626,14 @@ def main():
                     help="run a plain copy of a known size first (for counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write the traffic summary for --config from two counter passes")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("RESULTS_DB", "COMMAND"),
+                    help="write the kernel-trace summary for --config from a rocprofv3 database")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.config, *args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.config, *args.summarize_trace)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; the verify path is "

@@ -122,7 +122,7 @@ constexpr int kMaxSplits = 16;       // prefix splits per (sequence, KV head, ro
 #endif
 constexpr int kLongMinTiles = TV_LONG_MIN_TILES;
 constexpr int kMinSplitBlocks = 4;   // prefix blocks per split at least (when splitting)
-constexpr int kMaxOrderedPairs = 2048;  // pairs the ordering kernel ranks in one workgroup
+constexpr int kMaxOrderedPairs = 2048;  // pairs the ordering kernel ranks (all keys in one LDS)
 
 // Work items of a tree-attention launch.  Without a queue, workgroup i runs slot
 // i / 8 of die i % 8's list (the hardware hands workgroups to dies round-robin in

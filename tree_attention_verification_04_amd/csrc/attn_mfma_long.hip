@@ -771,59 +771,53 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
 // ranked by estimated cost, largest first (longest-processing-time-first list
 // scheduling: each free compute unit takes the next item of its die's list).
 // Cost of a pair = its tiles x its live 64-row units summed over its row tiles, from
-// the same clamped lengths the attention kernel uses.  One workgroup sorts the pairs
-// by cost, larger first, equal costs in index order.
-__global__ void __launch_bounds__(1024) k_attn_order(AttnArgs a, int* order) {
-  // key of pair p = cost << 32 | ~p: sorted descending, larger costs come first and
-  // equal costs in index order; padding keys are 0 and sort last
+// the same clamped lengths the attention kernel uses.  Key of pair p = cost << 32 |
+// ~p: keys are distinct, so the position of p in the list (larger costs first, equal
+// costs in index order) is the number of keys above its own.  Every workgroup puts
+// all keys in LDS and each of its threads counts for one pair; the counts read the
+// keys at one address per step across the wavefront (a broadcast, no bank
+// conflicts), so the ranks need no sort network and no barrier past the first.
+constexpr int kOrderThreads = 256;
+
+__device__ __forceinline__ uint64_t pair_cost_key(const AttnArgs& a, int p) {
+  const int b = p / a.hkv;
+  const int n0 = a.cu_nodes[b];
+  const int count = max(0, min(a.cu_nodes[b + 1] - n0, a.max_nodes));
+  const int plen = max(0, min(a.prefix_len[b], min(a.max_prefix, a.max_blocks * 64)));
+  const int tiles = (plen + kKT - 1) / kKT + (count + 63) / 64;
+  const int rows = a.group * count;
+  int units = 0;
+  for (int t = 0; t < a.row_tiles; ++t) {
+    const int live = rows - t * kMfmaRowsPerWG;
+    if (live > 0) units += (min(live, kMfmaRowsPerWG) + 63) / 64;
+  }
+  const uint32_t cost = static_cast<uint32_t>(tiles) * static_cast<uint32_t>(units);
+  return (static_cast<uint64_t>(cost) << 32) | static_cast<uint32_t>(~p);
+}
+
+__global__ void __launch_bounds__(kOrderThreads) k_attn_order(AttnArgs a, int* order) {
   __shared__ uint64_t s_key[kMaxOrderedPairs];
   const int pairs = a.batch * a.hkv;
-  int n2 = 2;
-  while (n2 < pairs) n2 <<= 1;
-  for (int p = threadIdx.x; p < n2; p += 1024) {
-    uint64_t key = 0;
-    if (p < pairs) {
-      const int b = p / a.hkv;
-      const int n0 = a.cu_nodes[b];
-      const int count = max(0, min(a.cu_nodes[b + 1] - n0, a.max_nodes));
-      const int plen = max(0, min(a.prefix_len[b], min(a.max_prefix, a.max_blocks * 64)));
-      const int tiles = (plen + kKT - 1) / kKT + (count + 63) / 64;
-      const int rows = a.group * count;
-      int units = 0;
-      for (int t = 0; t < a.row_tiles; ++t) {
-        const int live = rows - t * kMfmaRowsPerWG;
-        if (live > 0) units += (min(live, kMfmaRowsPerWG) + 63) / 64;
-      }
-      const uint32_t cost = static_cast<uint32_t>(tiles) * static_cast<uint32_t>(units);
-      key = (static_cast<uint64_t>(cost) << 32) | static_cast<uint32_t>(~p);
-    }
-    s_key[p] = key;
-  }
+  for (int p = threadIdx.x; p < pairs; p += kOrderThreads) s_key[p] = pair_cost_key(a, p);
   __syncthreads();
-  // bitonic sort, descending: blocks of size k merged by compare-exchange at
-  // distance j (log2(n2) (log2(n2) + 1) / 2 steps, one barrier each)
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += 1024) {
-        const int partner = i ^ j;
-        if (partner > i) {
-          const uint64_t x = s_key[i], y = s_key[partner];
-          const bool descending = (i & k) == 0;
-          if (descending ? x < y : x > y) {
-            s_key[i] = y;
-            s_key[partner] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  const int p = blockIdx.x * kOrderThreads + threadIdx.x;
+  if (p >= pairs) return;
+  const uint64_t mine = s_key[p];
+  int above = 0;
+  int i = 0;
+  for (; i + 4 <= pairs; i += 4) {
+    const uint64_t k0 = s_key[i], k1 = s_key[i + 1], k2 = s_key[i + 2], k3 = s_key[i + 3];
+    above += (k0 > mine) + (k1 > mine) + (k2 > mine) + (k3 > mine);
   }
-  for (int i = threadIdx.x; i < pairs; i += 1024)
-    order[i] = static_cast<int>(~static_cast<uint32_t>(s_key[i]));
+  for (; i < pairs; ++i) above += s_key[i] > mine;
+  order[above] = p;
 }
 
 int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s) {
-  hipLaunchKernelGGL(k_attn_order, dim3(1), dim3(1024), 0, s, a, order);
+  const int pairs = a.batch * a.hkv;
+  if (pairs < 1 || pairs > kMaxOrderedPairs) return TV_EINVAL;
+  hipLaunchKernelGGL(k_attn_order, dim3((pairs + kOrderThreads - 1) / kOrderThreads), dim3(kOrderThreads), 0,
+                     s, a, order);
   return check_launch("tree_verify_attention/order");
 }
 
