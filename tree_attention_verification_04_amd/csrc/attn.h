@@ -102,6 +102,10 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
 
 int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+// allow the matrix-core kernels' dynamic LDS on the current device (idempotent; the
+// launchers call them too, but a stream capture must not be the first caller)
+void set_attn_mfma_attributes();
+void set_attn_long_attributes();
 int launch_attn_long(const AttnArgs& a, hipStream_t s);
 int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s);
 int launch_attn_combine(const AttnArgs& a, hipStream_t s);

@@ -33,6 +33,8 @@
 // stage after the matrix work; one barrier per tile.  Work indices are remapped so
 // that the workgroups sharing a (sequence, KV head, split) land on the same XCD and
 // hit its L2 for the shared K/V tiles.
+#include <mutex>
+
 #include "mfma_tile.h"
 
 namespace tv {
@@ -555,17 +557,26 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
   if (a.lse != nullptr && d4 == 0) a.lse[gr] = w_sum > 0.0f ? mx + logf(w_sum) : -INFINITY;
 }
 
-int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_mfma<false, false>),
+void set_attn_mfma_attributes() {
+  // the dynamic LDS above 64 KB must be allowed once per function and device, before
+  // the first launch (and outside any stream capture)
+  static std::mutex mu;
+  static uint32_t done = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 32) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done & (1u << dev)) return;
+  const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_mfma<false, false>),
                           reinterpret_cast<const void*>(&k_attn_mfma<false, true>),
                           reinterpret_cast<const void*>(&k_attn_mfma<true, false>),
                           reinterpret_cast<const void*>(&k_attn_mfma<true, true>)};
-    for (const void* f : fns)
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
-    attr_set = true;
-  }
+  for (const void* f : fns)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+  done |= 1u << dev;
+}
+
+int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
+  set_attn_mfma_attributes();
   const bool fp8 = a.k_scale != nullptr, queued = a.queue != nullptr;
   const dim3 grid(queued ? kCUs : 8 * a.die_slots), block(kThreads);
   if (fp8 && queued)

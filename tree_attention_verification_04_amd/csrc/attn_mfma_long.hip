@@ -32,6 +32,8 @@
 // probabilities stay below 256 and most halves skip the rescale; the result is the
 // same softmax, normalised by the same running sum (the sum of the bf16
 // probabilities that enter the P.V product).
+#include <mutex>
+
 #include "mfma_tile.h"
 
 namespace tv {
@@ -49,6 +51,12 @@ constexpr int kAncOffL = kVOff + kRing * kTileBytes;
 constexpr int kMaskOff = kAncOffL + kRing * kAncSlotBytes;
 constexpr int kSmemL = kMaskOff + 64;
 constexpr int kLoadsPerIter = 5;      // per lane: 2 K chunks, 1 ancestor dword, 2 V chunks
+// A computing wavefront issues the K group of an iteration's loads after the first
+// score MFMA of the iteration's first half-step and the V group after the first of
+// the second, so the matrix cores have work while the loads are issued (serving
+// shapes 257-262 -> 253 us, others unchanged); a wavefront with no live rows issues
+// both groups at the start of the iteration.
+constexpr int kIssueAt = 0;
 static_assert(kWavesL * 32 == kMfmaRowsPerWG, "256 rows per workgroup");
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -58,18 +66,17 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)(p)));
 }
 
-// The loads of one iteration: K rows of one tile (2 x 16 B per lane, LDS lds_k and
-// lds_k + 8192), the ancestor dword of this lane's row (LDS lds_a), V rows of another
-// tile (LDS lds_v, lds_v + 8192).  Lane l of a load writes LDS at M0 + 16 l (4 l for
+// The loads of one iteration, in two groups: K rows of one tile (2 x 16 B per lane,
+// LDS lds_k and lds_k + 8192) with the ancestor dword of this lane's row (LDS lds_a);
+// V rows of another tile (LDS lds_v, lds_v + 8192).  Lane l of a load writes LDS at M0 + 16 l (4 l for
 // the dword); the global address is an SGPR base plus a per-lane 32-bit offset (an
 // instruction offset would move the LDS address too, so none is used).  Inline
 // assembly, so that the compiler does not see LDS stores it cannot order: every wait
 // on them is explicit (wait_loads_and_barrier).  M0 is saved and restored; one wait
 // state separates each M0 write from the load that reads it.
-__device__ __forceinline__ void issue_loads(const void* kb, uint32_t ko0, uint32_t ko1,
-                                            uint32_t lds_k, const void* ab, uint32_t ao,
-                                            uint32_t lds_a, const void* vb, uint32_t vo0,
-                                            uint32_t vo1, uint32_t lds_v) {
+__device__ __forceinline__ void issue_k_loads(const void* kb, uint32_t ko0, uint32_t ko1,
+                                              uint32_t lds_k, const void* ab, uint32_t ao,
+                                              uint32_t lds_a) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %[sv], m0\n\t"
@@ -82,6 +89,18 @@ __device__ __forceinline__ void issue_loads(const void* kb, uint32_t ko0, uint32
       "s_mov_b32 m0, %[la]\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dword %[a0], %[ab]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [k0] "v"(ko0), [k1] "v"(ko1), [kb] "s"(kb), [lk] "s"(lds_k), [a0] "v"(ao), [ab] "s"(ab),
+        [la] "s"(lds_a)
+      : "memory");
+}
+
+__device__ __forceinline__ void issue_v_loads(const void* vb, uint32_t vo0, uint32_t vo1,
+                                              uint32_t lds_v) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
       "s_mov_b32 m0, %[lv]\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %[v0], %[vb]\n\t"
@@ -90,8 +109,7 @@ __device__ __forceinline__ void issue_loads(const void* kb, uint32_t ko0, uint32
       "global_load_lds_dwordx4 %[v1], %[vb]\n\t"
       "s_mov_b32 m0, %[sv]"
       : [sv] "=&s"(saved)
-      : [k0] "v"(ko0), [k1] "v"(ko1), [kb] "s"(kb), [lk] "s"(lds_k), [a0] "v"(ao), [ab] "s"(ab),
-        [la] "s"(lds_a), [v0] "v"(vo0), [v1] "v"(vo1), [vb] "s"(vb), [lv] "s"(lds_v)
+      : [v0] "v"(vo0), [v1] "v"(vo1), [vb] "s"(vb), [lv] "s"(lds_v)
       : "memory");
 }
 
@@ -298,11 +316,17 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     return s;
   };
   // the loads of one iteration: K and ancestor words of the tile of sk, V of sv
+  auto issue_k = [&](const Src& sk, int slot_k) __attribute__((always_inline)) {
+    issue_k_loads(sk.k, sk.o0 + kcb, sk.o1 + kcb, lds_kv + slot_k * kTileBytes, anc_base, sk.anc,
+                  lds_anc + slot_k * kAncSlotBytes);
+  };
+  auto issue_v = [&](const Src& sv, int slot_v) __attribute__((always_inline)) {
+    issue_v_loads(sv.v, sv.o0 + vcb, sv.o1 + vcb, lds_kv + kVOff + slot_v * kTileBytes);
+  };
   auto issue = [&](const Src& sk, int slot_k, const Src& sv, int slot_v)
       __attribute__((always_inline)) {
-    issue_loads(sk.k, sk.o0 + kcb, sk.o1 + kcb, lds_kv + slot_k * kTileBytes, anc_base, sk.anc,
-                lds_anc + slot_k * kAncSlotBytes, sv.v, sv.o0 + vcb, sv.o1 + vcb,
-                lds_kv + kVOff + slot_v * kTileBytes);
+    issue_k(sk, slot_k);
+    issue_v(sv, slot_v);
   };
 
   // ---- FP8 pipeline: a tile's registers.  FP8 prefix tile: thread t holds the 16
@@ -481,7 +505,7 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     // takes the rescale factor and the sum of half h, and so do the accumulators,
     // which then wait for the P.V of half h.
     auto half_step = [&](f32x16_t& n, int ks, int hn, const uint32_t (&pp)[8], int vs, int hp,
-                         f32x16_t& c, uint32_t (&pc)[8], bool masked, uint32_t w)
+                         f32x16_t& c, uint32_t (&pc)[8], bool masked, uint32_t w, auto&& hook)
         __attribute__((always_inline)) {
       if (masked) mask(c, w);
       float mx = fmaxf(fmaxf(c[0], c[1]), c[2]);
@@ -551,6 +575,8 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         __builtin_amdgcn_sched_barrier(0);
         if ((r & 3) == 1) exp4(r >> 2);
         __builtin_amdgcn_sched_barrier(0);
+        if (r == kIssueAt) hook();
+        __builtin_amdgcn_sched_barrier(0);
       }
       l = l * al + sum;
       m_out = mr;
@@ -577,19 +603,29 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         store_regs(i + 2, (S + 2) % kRing, r);
         issue_anc(i + 3, (S + 3) % kRing);
         load_regs(i + 4, r);
-      } else {
-        const Src sk = tile_src(i + 3);
-        issue(sk, (S + 3) % kRing, sv, (S + 2) % kRing);
-        sv = sk;
+      }
+      Src sk{};
+      if constexpr (!kFp8) sk = tile_src(i + 3);
+      // the K group of this iteration's loads, then the V group (see kIssueAt)
+      const auto hk = [&]() __attribute__((always_inline)) {
+        if constexpr (!kFp8) issue_k(sk, (S + 3) % kRing);
+      };
+      const auto hv = [&]() __attribute__((always_inline)) {
+        if constexpr (!kFp8) issue_v(sv, (S + 2) % kRing);
+      };
+      if (!wave_live) {
+        hk();
+        hv();
       }
       if (wave_live) {
         uint32_t w = ~0u;
         const bool full = tile_vis(i, S, w);
         // probabilities of tile i half 0, scores of tile i half 1, P.V of tile i-1 half 1
-        half_step(s1, S, 1, px, (S + 3) % kRing, 1, s0, py, !full, w);
+        half_step(s1, S, 1, px, (S + 3) % kRing, 1, s0, py, !full, w, hk);
         // probabilities of tile i half 1, scores of tile i+1 half 0, P.V of tile i half 0
-        half_step(s0, (S + 1) % kRing, 0, py, S, 0, s1, px, !full, w >> 16);
+        half_step(s0, (S + 1) % kRing, 0, py, S, 0, s1, px, !full, w >> 16, hv);
       }
+      if constexpr (!kFp8) sv = sk;
       wait_loads_and_barrier<kLoadsPerIter>();
     };
 
@@ -741,17 +777,26 @@ __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
                  });
 }
 
-int launch_attn_long(const AttnArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_long<false, false>),
+void set_attn_long_attributes() {
+  // the dynamic LDS above 64 KB must be allowed once per function and device, before
+  // the first launch (and outside any stream capture)
+  static std::mutex mu;
+  static uint32_t done = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 32) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done & (1u << dev)) return;
+  const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_long<false, false>),
                           reinterpret_cast<const void*>(&k_attn_long<true, false>),
                           reinterpret_cast<const void*>(&k_attn_long<false, true>),
                           reinterpret_cast<const void*>(&k_attn_long<true, true>)};
-    for (const void* f : fns)
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
-    attr_set = true;
-  }
+  for (const void* f : fns)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
+  done |= 1u << dev;
+}
+
+int launch_attn_long(const AttnArgs& a, hipStream_t s) {
+  set_attn_long_attributes();
   const bool fp8 = a.k_scale != nullptr, queued = a.queue != nullptr;
   const dim3 grid(queued ? kCUs : 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits);
   if (queued && fp8)
