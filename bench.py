@@ -442,6 +442,54 @@ def cpu_baseline(case, budget_s: float):
                        "cores) + Python loops")
 
 
+def measure_uniforms(tv, case, dev, depth, reps: int) -> dict:
+    """tree_uniforms over the step's nodes (the counter-based acceptance and resample
+    uniforms), timed alone; bytes = 8 per node written."""
+    import torch
+    req = torch.arange(case.batch, dtype=torch.int64, device="cuda") + 1000
+    ua = torch.empty(case.total_nodes, dtype=torch.float32, device="cuda")
+    ur = torch.empty_like(ua)
+
+    def fn():
+        tv.tree_uniforms(req, depth, dev["cu_nodes"], seed=2026, step=1, u_accept=ua, u_resample=ur)
+
+    fn()
+    torch.cuda.synchronize()
+    us = graph_time_us(torch, fn, reps)
+    return {"us_per_launch": round(us, 3), "nodes": case.total_nodes}
+
+
+def measure_step_graph(tv, case, dev, replays: int) -> dict:
+    """The step through the library's own graph helper (tree_verify_graph_*): the three
+    calls captured once, replayed back to back between two events."""
+    import torch
+    step = tv.VerifyStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                         dev["prefix_len"], dev["k_tree"], dev["v_tree"], dev["parent"],
+                         dev["cu_nodes"], dev["p_target"], dev["p_draft"], dev["token"],
+                         dev["u_accept"], dev["u_resample"], max_nodes=max(1, case.max_nodes),
+                         max_prefix=case.max_prefix, max_path=16)
+    step.run()
+    torch.cuda.synchronize()
+    graph = step.capture()
+    try:
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            graph.launch(stream)
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        for _ in range(replays):
+            graph.launch(stream)
+        e_ev.record()
+        torch.cuda.synchronize()
+        if int(step.err.item()) != 0:
+            raise SystemExit(f"step graph: device error word {int(step.err.item())}")
+        us = s_ev.elapsed_time(e_ev) * 1e3 / replays
+    finally:
+        graph.close()
+    return {"us_per_step": round(us, 2), "replays": replays}
+
+
 def graph_time_us(torch, fn, reps: int, trials: int = 5) -> float:
     """Median over `trials` replays of a graph of `reps` back-to-back calls of fn,
     timed with events on the replay stream; microseconds per call."""
@@ -596,7 +644,9 @@ def measure_workload(torch, tv, config: int, args, headline: bool) -> dict:
         res["next_rows"] = {"kv_commit": measure_commit(tv, case, dev, acc_out, max_path, args.kernel_reps),
                             "softmax_rows": measure_softmax(tv, case, args.kernel_reps),
                             "fp8_kv_attention": fp8,
-                            "draft_tree": measure_draft_tree(tv, case, args.kernel_reps)}
+                            "draft_tree": measure_draft_tree(tv, case, args.kernel_reps),
+                            "uniforms": measure_uniforms(tv, case, dev, depth, args.kernel_reps),
+                            "step_graph": measure_step_graph(tv, case, dev, min(steps, 100))}
         res["measured_copy_GBps"] = measured_copy_gbps(torch)
     elif fp8 is not None:
         res["fp8_kv_attention"] = fp8

@@ -21,13 +21,19 @@
  *   tree_draft_build      draft top-K rows -> parent array of the candidate tree
  * and a fourth that follows them:
  *   tree_commit_kv        the accepted path's K/V become prefix positions
+ * and a counter-based generator of the acceptance uniforms:
+ *   tree_uniforms         per-node uniforms from (seed, request, tree level, node, step)
+ * The three calls of the step also come as one call and as a HIP graph:
+ *   tree_verify_step, tree_verify_graph_create / _launch / _destroy
  *
  * Conventions shared by every call
  *   - Every array pointer is DEVICE memory owned by the caller; the library
- *     keeps no pointer after a call returns.  The library allocates nothing:
- *     scratch comes from a caller-provided workspace whose size is returned
- *     by the matching *_workspace_size query (tree_accept_noalloc instead uses
- *     a fixed scratch array of the library, one per GPU).
+ *     keeps no pointer after a call returns (a graph made by
+ *     tree_verify_graph_create keeps those of its capture).  The library
+ *     allocates no device memory: scratch comes from a caller-provided
+ *     workspace whose size is returned by the matching *_workspace_size query
+ *     (tree_accept_noalloc instead uses a fixed scratch array of the library,
+ *     one per GPU; a graph handle is host memory plus the runtime's graph).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     work is enqueued on it; no call synchronises the device or the host.
  *     Buffers must stay alive until the stream has passed the call.
@@ -222,6 +228,31 @@ int tree_draft_build(const float* probs, const float* u, int32_t batch, int32_t 
                      void* stream);
 
 /*
+ * tree_uniforms — the acceptance and resample uniforms of every node from a
+ * counter-based generator ([P537] §8.2: every rank draws the same numbers for a
+ * node because they come from a stateless generator whose input is built from
+ * the request, the tree level, the node index and the step; nothing is broadcast,
+ * and a restarted request draws the same numbers).
+ *
+ * Generator: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11).  For local node j
+ * of sequence b: counter = (j, (uint32) depth[j], step, (uint64) request_id[b]),
+ * key = (seed, purpose); word 0 of the output block gives u_accept, word 1
+ * u_resample, each = (word >> 40) * 2^-24, exact in fp32, in [0, 1 - 2^-24].
+ * The values depend only on these inputs, not on the batch layout.
+ *
+ *   seed, purpose  key words (purpose separates independent draw families of a step)
+ *   step           decoding step
+ *   request_id     [batch] int64: the request that sequence b serves
+ *   depth          [total_nodes] int32, tree_build_index's output
+ *   cu_nodes       [batch + 1] int32
+ *   u_accept, u_resample  out [total_nodes] float; either may be NULL (not written)
+ * One thread per node; no workspace, no error bits.
+ */
+int tree_uniforms(uint64_t seed, uint64_t purpose, uint64_t step, const int64_t* request_id,
+                  const int32_t* depth, const int32_t* cu_nodes, int32_t batch,
+                  int32_t total_nodes, float* u_accept, float* u_resample, void* stream);
+
+/*
  * tree_accept — fused acceptance for every sequence, one launch, no host
  * round-trip ([P537] §2.2.3: per-node p_accept = min(1, p_target / p_draft), one
  * uniform per node, depth-first walk from the root cut at the first rejected
@@ -366,6 +397,97 @@ size_t tree_softmax_rows_workspace_size(int32_t ctx_rows, int32_t vocab);
 int tree_softmax_rows(const float* logits, int32_t ctx_rows, int32_t vocab, const int32_t* row_of,
                       int32_t rows, float inv_temperature, float* probs, void* workspace,
                       size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * tree_verify_step — the step's three calls in one: tree_build_index, then
+ * tree_verify_attention, then tree_accept, enqueued in that order on `stream`
+ * with the arguments below (each field means what the same-named argument of
+ * those calls means; anc_bits/words/depth link the first to the other two).
+ * Returns the first non-TV_OK status of the three; the calls before the
+ * failing one are then already enqueued.
+ *
+ * tree_verify_graph_create — captures the same three calls once into a HIP
+ * graph (a stream capture; [ViSpec] §3.2: the whole verification flow is
+ * captured in a graph so that no host code runs between its kernels) and
+ * instantiates it.  The graph holds the pointers and sizes of `args` as they are
+ * at capture: every replay reads and writes those same buffers, so the caller
+ * refreshes the inputs in place between replays.  `stream` (NULL: a temporary
+ * stream of the library) is used for the capture only; nothing executes.  The
+ * handle and the runtime's graph objects are the only allocations (host side, and
+ * whatever the HIP runtime needs for an executable graph).
+ * tree_verify_graph_launch — replays the graph on `stream` (any stream of the
+ * same device); replays of one graph, or of graphs sharing a workspace, must not
+ * overlap on the device.
+ * tree_verify_graph_destroy — releases the handle (NULL is ignored); the caller
+ * makes sure no replay is still running.
+ */
+typedef struct tree_verify_step_args {
+  /* tree_build_index */
+  const int32_t* parent;
+  const int32_t* cu_nodes;
+  int32_t batch;
+  int32_t total_nodes;
+  int32_t max_nodes;
+  int32_t words;
+  const int32_t* prefix_len;
+  uint64_t* anc_bits;
+  int32_t* depth;
+  int32_t* pos; /* may be NULL */
+  /* tree_verify_attention */
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_prefix;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t dtype;
+  float softmax_scale;
+  const void* k_tree;
+  const void* v_tree;
+  void* out;
+  float* lse; /* may be NULL */
+  void* attn_workspace;
+  size_t attn_workspace_bytes;
+  /* tree_accept */
+  const float* p_target;
+  const float* p_draft;
+  const int32_t* token;
+  const float* u_accept;
+  const float* u_resample;
+  const float* p_own;      /* may be NULL */
+  const int32_t* own_row;  /* may be NULL */
+  int32_t own_rows;
+  int32_t vocab;
+  int32_t max_path;
+  int32_t reserved; /* 0 */
+  int32_t* accept_len;
+  int32_t* path;
+  int32_t* resample_node;
+  int32_t* resample_token;
+  uint8_t* node_ok; /* may be NULL */
+  void* accept_workspace;
+  size_t accept_workspace_bytes;
+  /* all three */
+  int32_t* err;
+} tree_verify_step_args;
+
+typedef struct tree_verify_graph tree_verify_graph; /* opaque */
+
+/* sizeof(tree_verify_step_args) as compiled into the library (a binding checks it) */
+size_t tree_verify_step_args_size(void);
+
+int tree_verify_step(const tree_verify_step_args* args, void* stream);
+
+int tree_verify_graph_create(const tree_verify_step_args* args, void* stream,
+                             tree_verify_graph** graph);
+
+int tree_verify_graph_launch(tree_verify_graph* graph, void* stream);
+
+int tree_verify_graph_destroy(tree_verify_graph* graph);
 
 /* Reason for the last non-TV_OK status on the calling thread ("" if none). */
 const char* tree_last_error(void);

@@ -245,3 +245,33 @@ def test_softmax_rows_host_checks(lib):
     assert call(wsb=8) == tv.TV_EWORKSPACE
     assert call(r=0, c=0) == tv.TV_OK                # nothing to do
     assert tv.TV_ERR_ROW == oracle.probs.ERR_ROW
+
+
+def test_uniforms_host_checks(lib):
+    one = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    assert lib.tree_uniforms(1, 0, 0, one, one, one, -1, 4, one, one, None) == tv.TV_EINVAL
+    assert lib.tree_uniforms(1, 0, 0, one, one, one, 1, -4, one, one, None) == tv.TV_EINVAL
+    assert lib.tree_uniforms(1, 0, 0, one, one, one, 0, 4, one, one, None) == tv.TV_EINVAL
+    assert lib.tree_uniforms(1, 0, 0, None, one, one, 1, 4, one, one, None) == tv.TV_EINVAL
+    assert b"request_id" in lib.tree_last_error()
+    assert lib.tree_uniforms(1, 0, 0, one, None, one, 1, 4, one, one, None) == tv.TV_EINVAL
+    # nothing to do: no nodes, or no output asked for
+    assert lib.tree_uniforms(1, 0, 0, None, None, None, 0, 0, None, None, None) == tv.TV_OK
+    assert lib.tree_uniforms(1, 0, 0, one, one, one, 1, 4, None, None, None) == tv.TV_OK
+    # 64-bit key and counter words pass through the ABI unchanged
+    assert lib.tree_uniforms(2**64 - 1, 2**63, 2**64 - 1, one, one, one, 1, 0, one, one, None) == tv.TV_OK
+
+
+def test_step_and_graph_host_checks(lib):
+    assert lib.tree_verify_step_args_size() == ctypes.sizeof(tv.StepArgs)
+    assert lib.tree_verify_step(None, None) == tv.TV_EINVAL
+    h = ctypes.c_void_p()
+    assert lib.tree_verify_graph_create(None, None, ctypes.byref(h)) == tv.TV_EINVAL
+    assert lib.tree_verify_graph_create(ctypes.byref(tv.StepArgs()), None, None) == tv.TV_EINVAL
+    assert lib.tree_verify_graph_launch(None, None) == tv.TV_EINVAL
+    assert lib.tree_verify_graph_destroy(None) == tv.TV_OK
+    # a step whose first call fails its host checks enqueues nothing
+    a = tv.StepArgs()
+    a.batch, a.total_nodes, a.max_nodes, a.words = 1, 4, 0, 1
+    assert lib.tree_verify_step(ctypes.byref(a), None) == tv.TV_EUNSUPPORTED
+    assert b"max_nodes" in lib.tree_last_error()

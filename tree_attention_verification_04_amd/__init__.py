@@ -48,6 +48,12 @@ EXPORTS = (
     "tree_commit_kv",
     "tree_softmax_rows_workspace_size",
     "tree_softmax_rows",
+    "tree_uniforms",
+    "tree_verify_step_args_size",
+    "tree_verify_step",
+    "tree_verify_graph_create",
+    "tree_verify_graph_launch",
+    "tree_verify_graph_destroy",
     "tree_last_error",
 )
 
@@ -58,6 +64,24 @@ class TreeVerifyError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__(f"{fn} failed with status {status}: {msg}")
         self.status = status
+
+
+class StepArgs(ctypes.Structure):
+    """tree_verify_step_args of treeverify.h, field for field."""
+    _P, _I = ctypes.c_void_p, ctypes.c_int32
+    _fields_ = [
+        ("parent", _P), ("cu_nodes", _P), ("batch", _I), ("total_nodes", _I), ("max_nodes", _I),
+        ("words", _I), ("prefix_len", _P), ("anc_bits", _P), ("depth", _P), ("pos", _P),
+        ("q", _P), ("k_cache", _P), ("v_cache", _P), ("block_table", _P), ("num_blocks", _I),
+        ("max_blocks", _I), ("max_prefix", _I), ("hq", _I), ("hkv", _I), ("head_dim", _I),
+        ("dtype", _I), ("softmax_scale", ctypes.c_float), ("k_tree", _P), ("v_tree", _P),
+        ("out", _P), ("lse", _P), ("attn_workspace", _P), ("attn_workspace_bytes", ctypes.c_size_t),
+        ("p_target", _P), ("p_draft", _P), ("token", _P), ("u_accept", _P), ("u_resample", _P),
+        ("p_own", _P), ("own_row", _P), ("own_rows", _I), ("vocab", _I), ("max_path", _I),
+        ("reserved", _I), ("accept_len", _P), ("path", _P), ("resample_node", _P),
+        ("resample_token", _P), ("node_ok", _P), ("accept_workspace", _P),
+        ("accept_workspace_bytes", ctypes.c_size_t), ("err", _P),
+    ]
 
 
 def _declare(lib: ctypes.CDLL) -> None:
@@ -90,6 +114,21 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_softmax_rows_workspace_size.restype = Z
     lib.tree_softmax_rows.argtypes = [P, I, I, P, I, F, P, P, Z, P, P]
     lib.tree_softmax_rows.restype = ctypes.c_int
+    U64 = ctypes.c_uint64
+    lib.tree_uniforms.argtypes = [U64, U64, U64, P, P, P, I, I, P, P, P]
+    lib.tree_uniforms.restype = ctypes.c_int
+    lib.tree_verify_step_args_size.argtypes = []
+    lib.tree_verify_step_args_size.restype = Z
+    lib.tree_verify_step.argtypes = [ctypes.POINTER(StepArgs), P]
+    lib.tree_verify_step.restype = ctypes.c_int
+    lib.tree_verify_graph_create.argtypes = [ctypes.POINTER(StepArgs), P, ctypes.POINTER(P)]
+    lib.tree_verify_graph_create.restype = ctypes.c_int
+    lib.tree_verify_graph_launch.argtypes = [P, P]
+    lib.tree_verify_graph_launch.restype = ctypes.c_int
+    lib.tree_verify_graph_destroy.argtypes = [P]
+    lib.tree_verify_graph_destroy.restype = ctypes.c_int
+    if lib.tree_verify_step_args_size() != ctypes.sizeof(StepArgs):
+        raise RuntimeError("tree_verify_step_args layout differs between the library and the binding")
     lib.tree_last_error.argtypes = []
     lib.tree_last_error.restype = ctypes.c_char_p
 
@@ -500,3 +539,159 @@ def tree_softmax_rows(logits, row_of=None, *, inv_temperature: float = 1.0, prob
                                  float(inv_temperature), _ptr(probs), _ptr(workspace),
                                  workspace.numel(), _ptr(err), _stream(stream)))
     return probs, err
+
+
+def tree_uniforms(request_id, depth, cu_nodes, *, seed: int, step: int, purpose: int = 0,
+                  u_accept=None, u_resample=None, stream=None):
+    """Acceptance and resample uniforms of every node from the counter-based generator
+    (Philox4x64-10 keyed by (seed, purpose), counter = (local node, depth, step,
+    request_id[b])).  Returns (u_accept, u_resample), float32 [total_nodes]."""
+    lib = load()
+    _need(request_id, "request_id", torch.int64, 1)
+    _need(depth, "depth", torch.int32, 1)
+    _need(cu_nodes, "cu_nodes", torch.int32, 1)
+    batch, total = request_id.numel(), depth.numel()
+    if cu_nodes.numel() != batch + 1:
+        raise ValueError("cu_nodes must hold batch + 1 entries")
+    if u_accept is None:
+        u_accept = torch.empty(total, dtype=torch.float32, device=depth.device)
+    if u_resample is None:
+        u_resample = torch.empty(total, dtype=torch.float32, device=depth.device)
+    for t, name in ((u_accept, "u_accept"), (u_resample, "u_resample")):
+        _need(t, name, torch.float32, 1)
+        if t.numel() != total:
+            raise ValueError(f"{name} must hold total_nodes entries")
+    mask = (1 << 64) - 1
+    _check("tree_uniforms",
+           lib.tree_uniforms(int(seed) & mask, int(purpose) & mask, int(step) & mask,
+                             _ptr(request_id), _ptr(depth), _ptr(cu_nodes), batch, total,
+                             _ptr(u_accept), _ptr(u_resample), _stream(stream)))
+    return u_accept, u_resample
+
+
+class VerifyStep:
+    """The step's buffers bound once: run() enqueues tree_verify_step (index, attention,
+    acceptance); capture() returns a VerifyGraph that replays the same three calls on
+    the same buffers (refresh inputs in place between replays).  Outputs: anc, depth,
+    out, lse (if want_lse), accept (dict as tree_accept returns), err."""
+
+    def __init__(self, q, k_cache, v_cache, block_table, prefix_len, k_tree, v_tree, parent,
+                 cu_nodes, p_target, p_draft, token, u_accept, u_resample, *, max_nodes: int,
+                 max_prefix: int, max_path: int, scale: float | None = None, p_own=None,
+                 own_row=None, want_lse: bool = False):
+        lib = load()
+        fdt = (torch.float32, torch.bfloat16)
+        _need(q, "q", fdt, 3)
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            _need(t, name, q.dtype, 4)
+        for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+            _need(t, name, q.dtype, 3)
+        for name, t in (("block_table", block_table),):
+            _need(t, name, torch.int32, 2)
+        for name, t in (("prefix_len", prefix_len), ("parent", parent), ("cu_nodes", cu_nodes),
+                        ("token", token)):
+            _need(t, name, torch.int32, 1)
+        for name, t in (("p_target", p_target), ("p_draft", p_draft)):
+            _need(t, name, torch.float32, 2)
+        for name, t in (("u_accept", u_accept), ("u_resample", u_resample)):
+            _need(t, name, torch.float32, 1)
+        if (p_own is None) != (own_row is None):
+            raise ValueError("p_own and own_row go together")
+        total, hq, d = q.shape
+        num_blocks, hkv, blk, d2 = k_cache.shape
+        if blk != TV_BLOCK or d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("k_cache/v_cache must be [num_blocks, hkv, 64, head_dim]")
+        if tuple(k_tree.shape) != (total, hkv, d) or tuple(v_tree.shape) != (total, hkv, d):
+            raise ValueError("k_tree/v_tree must be [total_nodes, hkv, head_dim]")
+        batch = cu_nodes.numel() - 1
+        vocab = p_target.shape[1]
+        if tuple(p_target.shape) != (total, vocab) or tuple(p_draft.shape) != (total, vocab):
+            raise ValueError("p_target/p_draft must be [total_nodes, vocab]")
+        if block_table.shape[0] != batch or prefix_len.numel() != batch:
+            raise ValueError("block_table / prefix_len must have one row per sequence")
+        for t in (parent, token, u_accept, u_resample):
+            if t.numel() != total:
+                raise ValueError("parent, token, u_accept and u_resample need one entry per node")
+        own_rows = 0
+        if p_own is not None:
+            _need(p_own, "p_own", torch.float32, 2)
+            _need(own_row, "own_row", torch.int32, 1)
+            if p_own.shape[1] != vocab or own_row.numel() != total:
+                raise ValueError("p_own must be [rows, vocab] and own_row [total_nodes]")
+            own_rows = p_own.shape[0]
+        dev, dt = q.device, dtype_code(q.dtype)
+        words = (max_nodes + 63) // 64
+        self.anc = torch.empty((total, words), dtype=torch.int64, device=dev)
+        self.depth = torch.empty(total, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((total, hq), dtype=torch.float32, device=dev) if want_lse else None
+        self.accept = dict(accept_len=torch.empty(batch, dtype=torch.int32, device=dev),
+                           path=torch.empty((batch, max_path), dtype=torch.int32, device=dev),
+                           resample_node=torch.empty(batch, dtype=torch.int32, device=dev),
+                           resample_token=torch.empty(batch, dtype=torch.int32, device=dev),
+                           node_ok=torch.empty(total, dtype=torch.uint8, device=dev))
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.accept["err"] = self.err
+        need_a = tree_verify_attention_workspace_size(batch, total, max_nodes, max_prefix, hq, hkv, d, dt)
+        self.attn_ws = torch.zeros(max(need_a, 1), dtype=torch.uint8, device=dev)  # kept zero
+        need_c = tree_accept_workspace_size(batch, vocab)
+        self.accept_ws = torch.zeros(max(need_c, 1), dtype=torch.uint8, device=dev)  # kept zero
+        # every tensor the struct points at stays referenced by this object
+        self._keep = (q, k_cache, v_cache, block_table, prefix_len, k_tree, v_tree, parent,
+                      cu_nodes, p_target, p_draft, token, u_accept, u_resample, p_own, own_row)
+        a = StepArgs()
+        p = lambda t: None if t is None else t.data_ptr()
+        a.parent, a.cu_nodes, a.batch, a.total_nodes = p(parent), p(cu_nodes), batch, total
+        a.max_nodes, a.words, a.prefix_len = max_nodes, words, p(prefix_len)
+        a.anc_bits, a.depth, a.pos = p(self.anc), p(self.depth), None
+        a.q, a.k_cache, a.v_cache, a.block_table = p(q), p(k_cache), p(v_cache), p(block_table)
+        a.num_blocks, a.max_blocks, a.max_prefix = num_blocks, block_table.shape[1], max_prefix
+        a.hq, a.hkv, a.head_dim, a.dtype = hq, hkv, d, dt
+        a.softmax_scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        a.k_tree, a.v_tree, a.out, a.lse = p(k_tree), p(v_tree), p(self.out), p(self.lse)
+        a.attn_workspace, a.attn_workspace_bytes = p(self.attn_ws), self.attn_ws.numel()
+        a.p_target, a.p_draft, a.token = p(p_target), p(p_draft), p(token)
+        a.u_accept, a.u_resample, a.p_own, a.own_row = p(u_accept), p(u_resample), p(p_own), p(own_row)
+        a.own_rows, a.vocab, a.max_path, a.reserved = own_rows, vocab, max_path, 0
+        o = self.accept
+        a.accept_len, a.path = p(o["accept_len"]), p(o["path"])
+        a.resample_node, a.resample_token, a.node_ok = (p(o["resample_node"]), p(o["resample_token"]),
+                                                        p(o["node_ok"]))
+        a.accept_workspace, a.accept_workspace_bytes = p(self.accept_ws), self.accept_ws.numel()
+        a.err = p(self.err)
+        self.args = a
+        self._lib = lib
+
+    def run(self, stream=None) -> None:
+        _check("tree_verify_step", self._lib.tree_verify_step(ctypes.byref(self.args), _stream(stream)))
+
+    def capture(self, stream=None) -> "VerifyGraph":
+        return VerifyGraph(self, stream)
+
+
+class VerifyGraph:
+    """A HIP graph of one VerifyStep's three calls (tree_verify_graph_*)."""
+
+    def __init__(self, step: VerifyStep, stream=None):
+        self._lib, self.step = step._lib, step
+        h = ctypes.c_void_p()
+        s = ctypes.c_void_p(None) if stream is None else _stream(stream)
+        _check("tree_verify_graph_create",
+               self._lib.tree_verify_graph_create(ctypes.byref(step.args), s, ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        if self._h is None:
+            raise RuntimeError("graph already destroyed")
+        _check("tree_verify_graph_launch", self._lib.tree_verify_graph_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if self._h is not None:
+            _check("tree_verify_graph_destroy", self._lib.tree_verify_graph_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
