@@ -342,7 +342,7 @@ def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict 
     return dict(us_per_launch=round(us, 3), bf16_us_per_launch=round(bf16_us, 3),
                 alg_bytes=int(bytes_), achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm",
-                kernel="register-staged matrix-core kernel (dequantizes into LDS)")
+                kernel="matrix-core kernels: E4M3 tiles through registers, dequantized into the bf16 LDS rings")
 
 
 def measure_draft_tree(tv, case, reps: int) -> dict:
