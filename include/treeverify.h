@@ -191,6 +191,23 @@ int tree_verify_attention_fp8kv(const void* q, const uint8_t* k_cache, const uin
                                 int32_t* err, void* stream);
 
 /*
+ * tree_quantize_rows_e4m3 — rows of 128 elements to OCP E4M3 codes with one
+ * power-of-two scale per row ([P537] §9.2: Q, K, V in FP8 E4M3 with one scale per
+ * 128 elements), the format tree_verify_attention_fp8 reads.
+ *
+ * Row i with amax = max |x[i][:]| gets the smallest power of two 2^s with
+ * amax <= 448 * 2^s (s in [-127, 127]; s = 0 for an all-zero row), stored as the
+ * E8M0 byte exps[i] = s + 127; codes[i][d] = round-to-nearest-even E4M3 of
+ * x[i][d] * 2^-s (exact product; the sign of zero is kept).  Dequantized value:
+ * e4m3(code) * 2^(exps - 127).
+ *
+ *   x      [rows, 128] dtype (TV_DTYPE_BF16 or TV_DTYPE_F32), 16-byte aligned
+ *   codes  out [rows, 128] uint8; exps out [rows] uint8
+ */
+int tree_quantize_rows_e4m3(const void* x, int32_t dtype, int64_t rows, uint8_t* codes,
+                            uint8_t* exps, void* stream);
+
+/*
  * tree_draft_build — the candidate tree of each sequence from the draft model's
  * top-K rows, before the step: importance-sampled expansion ([P500] §3.1: weights
  * w = p^beta / sum p^beta over a context's top-K, branches kept and deepened by

@@ -49,6 +49,7 @@ EXPORTS = (
     "tree_softmax_rows_workspace_size",
     "tree_softmax_rows",
     "tree_uniforms",
+    "tree_quantize_rows_e4m3",
     "tree_verify_step_args_size",
     "tree_verify_step",
     "tree_verify_graph_create",
@@ -117,6 +118,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     U64 = ctypes.c_uint64
     lib.tree_uniforms.argtypes = [U64, U64, U64, P, P, P, I, I, P, P, P]
     lib.tree_uniforms.restype = ctypes.c_int
+    lib.tree_quantize_rows_e4m3.argtypes = [P, I, ctypes.c_int64, P, P, P]
+    lib.tree_quantize_rows_e4m3.restype = ctypes.c_int
     lib.tree_verify_step_args_size.argtypes = []
     lib.tree_verify_step_args_size.restype = Z
     lib.tree_verify_step.argtypes = [ctypes.POINTER(StepArgs), P]
@@ -695,3 +698,26 @@ class VerifyGraph:
             self.close()
         except Exception:
             pass
+
+
+def tree_quantize_rows_e4m3(x, *, codes=None, exps=None, stream=None):
+    """Rows of 128 elements (x [..., 128], bf16 or float32) to E4M3 codes with one
+    power-of-two scale per row.  Returns (codes [..., 128] uint8, exps [...] uint8:
+    value = e4m3(code) * 2^(exps - 127))."""
+    lib = load()
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    if x.shape[-1] != 128:
+        raise ValueError("rows must hold 128 elements")
+    rows = x.numel() // 128
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty(x.shape[:-1], dtype=torch.uint8, device=x.device)
+    _need(codes, "codes", torch.uint8)
+    _need(exps, "exps", torch.uint8)
+    if codes.numel() != x.numel() or exps.numel() != rows:
+        raise ValueError("codes must match x and exps hold one byte per row")
+    _check("tree_quantize_rows_e4m3",
+           lib.tree_quantize_rows_e4m3(_ptr(x), dtype_code(x.dtype), rows, _ptr(codes), _ptr(exps),
+                                       _stream(stream)))
+    return codes, exps
