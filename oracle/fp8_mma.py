@@ -15,9 +15,10 @@ Readings taken where the page leaves the step open (each also in the design note
   * Quantizing a row x (fp32 values): amax = max |x|; its scale is the smallest
     power of two 2^s with amax <= 448 * 2^s (448 = largest finite E4M3), s in
     [-127, 127]; an all-zero row takes s = 0.  Codes = round-to-nearest-even of
-    x * 2^-s to E4M3 (the product is exact).  Q and the tree's K/V, which the
-    step receives in bf16, are quantized this way; the paged cache arrives as
-    codes and exponent bytes.
+    x * 2^-s to E4M3 (the product is exact).  K and V, the paged prefix and the
+    tree's own rows alike, arrive in this format (codes and exponent bytes: the
+    forward pass that writes the FP8 cache writes the tree's K/V the same way);
+    Q arrives in bf16 and is quantized by this rule inside the step.
   * Attention is then the plain definition (oracle.attention) over the
     dequantized values, code value * 2^s, in fp64.
 
@@ -102,12 +103,14 @@ def round_trip(x) -> np.ndarray:
     return dequantize_rows(*quantize_rows(x))
 
 
-def tree_attention_fp8mma(q, k8, v8, k_exp, v_exp, block_table, prefix_len, k_tree, v_tree,
-                          cu_nodes, parent, hq: int, hkv: int, scale: float, nodes=None):
-    """Tree attention with Q, K and V in E4M3 and E8M0 row scales: q [total, hq, 128],
-    k_tree / v_tree [total, hkv, 128] are the fp32 values of the bf16 inputs and are
-    quantized per row; k8 / v8 [num_blocks, hkv, 64, 128] codes with k_exp / v_exp
-    [num_blocks, hkv, 64] exponent bytes are the paged cache."""
+def tree_attention_fp8mma(q, k8, v8, k_exp, v_exp, block_table, prefix_len, kt8, vt8, kt_exp,
+                          vt_exp, cu_nodes, parent, hq: int, hkv: int, scale: float, nodes=None):
+    """Tree attention with Q, K and V in E4M3 and E8M0 row scales: q [total, hq, 128]
+    are the fp32 values of the bf16 queries, quantized per row here; k8 / v8
+    [num_blocks, hkv, 64, 128] with k_exp / v_exp [num_blocks, hkv, 64] are the paged
+    cache, kt8 / vt8 [total, hkv, 128] with kt_exp / vt_exp [total, hkv] the tree's
+    K/V, all as codes and exponent bytes."""
     return tree_attention(round_trip(q), dequantize_rows(k8, k_exp), dequantize_rows(v8, v_exp),
-                          block_table, prefix_len, round_trip(k_tree), round_trip(v_tree), cu_nodes,
-                          parent, hq, hkv, scale, nodes=nodes)
+                          block_table, prefix_len, dequantize_rows(kt8, kt_exp),
+                          dequantize_rows(vt8, vt_exp), cu_nodes, parent, hq, hkv, scale,
+                          nodes=nodes)

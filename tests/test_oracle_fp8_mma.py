@@ -110,14 +110,15 @@ def test_exact_inputs_reduce_to_the_fp32_scale_oracle_and_plain_attention():
     parent = np.array([-1, 0, 0, 1, -1], np.int32)
     cu = np.array([0, 5], np.int32)
     q, _, _ = rows((5, hq))
-    kt, _, _ = rows((5, hkv))
-    vt, _, _ = rows((5, hkv))
+    kt, kt8, kte = rows((5, hkv))
+    vt, vt8, vte = rows((5, hkv))
     _, k8, ke = rows((nb, hkv, 64))
     _, v8, ve = rows((nb, hkv, 64))
     bt = np.array([[2, 0, 1]], np.int32)
     plen = np.array([150], np.int32)
     scale = 1.0 / np.sqrt(128.0)
-    got = M.tree_attention_fp8mma(q, k8, v8, ke, ve, bt, plen, kt, vt, cu, parent, hq, hkv, scale)
+    got = M.tree_attention_fp8mma(q, k8, v8, ke, ve, bt, plen, kt8, vt8, kte, vte, cu, parent, hq, hkv,
+                                  scale)
     ks = np.exp2(ke.astype(np.float64) - 127)
     vs = np.exp2(ve.astype(np.float64) - 127)
     want = oracle.tree_attention_fp8(q.astype(np.float64), k8, v8, ks, vs, bt, plen, kt.astype(np.float64),
@@ -143,7 +144,10 @@ def test_quantization_error_is_what_separates_it_from_plain_attention():
     v8, ve = M.quantize_rows(rng.normal(0, 1, (2, hkv, 64, 128)).astype(np.float32))
     bt = np.array([[1, 0]], np.int32)
     plen = np.array([100], np.int32)
-    got = M.tree_attention_fp8mma(q, k8, v8, ke, ve, bt, plen, kt, vt, cu, parent, hq, hkv, 0.1)
+    kt8, kte = M.quantize_rows(kt)
+    vt8, vte = M.quantize_rows(vt)
+    got = M.tree_attention_fp8mma(q, k8, v8, ke, ve, bt, plen, kt8, vt8, kte, vte, cu, parent, hq, hkv,
+                                  0.1)
     want = oracle.tree_attention(M.round_trip(q), M.dequantize_rows(k8, ke), M.dequantize_rows(v8, ve),
                                  bt, plen, M.round_trip(kt), M.round_trip(vt), cu, parent, hq, hkv, 0.1)
     np.testing.assert_array_equal(got[0], want[0])
