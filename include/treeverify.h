@@ -15,8 +15,9 @@
  *   tree_verify_attention every tree node attends to the shared paged prefix
  *                         and to its own ancestors (mask M_tree)
  *   tree_accept           ratio test, longest accepted path, residual resample
- * a variant of the second for an FP8 prefix cache:
- *   tree_verify_attention_fp8kv
+ * two variants of the second for an FP8 cache:
+ *   tree_verify_attention_fp8kv   (E4M3 prefix with fp32 row scales, exact q)
+ *   tree_verify_attention_fp8     (E4M3 Q, K, V with power-of-two row scales, FP8 matrix cores)
  * one that builds the tree before them:
  *   tree_draft_build      draft top-K rows -> parent array of the candidate tree
  * and a fourth that follows them:
@@ -206,6 +207,43 @@ int tree_verify_attention_fp8kv(const void* q, const uint8_t* k_cache, const uin
  */
 int tree_quantize_rows_e4m3(const void* x, int32_t dtype, int64_t rows, uint8_t* codes,
                             uint8_t* exps, void* stream);
+
+/*
+ * tree_verify_attention_fp8 — tree attention on the FP8 matrix cores: Q, K and V in
+ * OCP E4M3 with one power-of-two scale per 128-element row ([P537] §9.2: Q, K, V
+ * in FP8 E4M3 with block scaling, one scale per 128 elements, fp32 accumulation).
+ *
+ * K and V, of the paged prefix and of the tree alike, arrive as E4M3 codes with one
+ * E8M0 exponent byte per row (value = e4m3(code) * 2^(e - 127), as
+ * tree_quantize_rows_e4m3 writes it: the forward pass that writes the FP8 cache
+ * writes the tree's rows the same way).  q arrives in bf16 and is quantized by the
+ * same rule inside the call.  The scores Q.K run on the scaled FP8 matrix
+ * instructions (the row exponents applied by the hardware); V is converted exactly
+ * to bf16 and P.V runs in bf16 as in tree_verify_attention.  The result is
+ * tree_verify_attention's on the dequantized Q, K and V (within its bf16 tolerance).
+ *
+ *   k_cache/v_cache [num_blocks, hkv, 64, 128] uint8 (E4M3)
+ *   k_exp/v_exp     [num_blocks, hkv, 64] uint8 (E8M0; may be NULL when max_prefix == 0)
+ *   k_tree/v_tree   [total_nodes, hkv, 128] uint8 (E4M3)
+ *   kt_exp/vt_exp   [total_nodes, hkv] uint8 (E8M0)
+ *   everything else as for tree_verify_attention with head_dim 128, bf16 q and out;
+ *   workspace >= tree_verify_attention_fp8_workspace_size(...), zero-filled before its
+ *   first use as there
+ */
+size_t tree_verify_attention_fp8_workspace_size(int32_t batch, int32_t total_nodes,
+                                                int32_t max_nodes, int32_t max_prefix, int32_t hq,
+                                                int32_t hkv);
+
+int tree_verify_attention_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                              const uint8_t* k_exp, const uint8_t* v_exp, int32_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* prefix_len, const uint8_t* k_tree,
+                              const uint8_t* v_tree, const uint8_t* kt_exp, const uint8_t* vt_exp,
+                              const int32_t* cu_nodes, const uint64_t* anc_bits, int32_t words,
+                              int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                              int32_t max_prefix, int32_t hq, int32_t hkv, float softmax_scale,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              int32_t* err, void* stream);
 
 /*
  * tree_draft_build — the candidate tree of each sequence from the draft model's

@@ -41,6 +41,8 @@ EXPORTS = (
     "tree_verify_attention",
     "tree_verify_attention_fp8kv_workspace_size",
     "tree_verify_attention_fp8kv",
+    "tree_verify_attention_fp8_workspace_size",
+    "tree_verify_attention_fp8",
     "tree_draft_build",
     "tree_accept_workspace_size",
     "tree_accept",
@@ -99,6 +101,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_attention_fp8kv.argtypes = [P, P, P, P, P, I, P, I, P, P, P, P, P, I, I, I, I,
                                                 I, I, I, F, P, P, P, Z, P, P]
     lib.tree_verify_attention_fp8kv.restype = ctypes.c_int
+    lib.tree_verify_attention_fp8_workspace_size.argtypes = [I] * 6
+    lib.tree_verify_attention_fp8_workspace_size.restype = Z
+    lib.tree_verify_attention_fp8.argtypes = [P, P, P, P, P, I, P, I, P, P, P, P, P, P, P, I, I,
+                                              I, I, I, I, I, F, P, P, P, Z, P, P]
+    lib.tree_verify_attention_fp8.restype = ctypes.c_int
     lib.tree_draft_build.argtypes = [P, P, I, I, I, I, I, F, F, P, P, P, P, P, P]
     lib.tree_draft_build.restype = ctypes.c_int
     lib.tree_accept_workspace_size.argtypes = [I, I]
@@ -721,3 +728,63 @@ def tree_quantize_rows_e4m3(x, *, codes=None, exps=None, stream=None):
            lib.tree_quantize_rows_e4m3(_ptr(x), dtype_code(x.dtype), rows, _ptr(codes), _ptr(exps),
                                        _stream(stream)))
     return codes, exps
+
+
+def tree_verify_attention_fp8_workspace_size(batch, total_nodes, max_nodes, max_prefix, hq,
+                                             hkv) -> int:
+    return int(load().tree_verify_attention_fp8_workspace_size(batch, total_nodes, max_nodes,
+                                                               max_prefix, hq, hkv))
+
+
+def tree_verify_attention_fp8(q, k_cache, v_cache, k_exp, v_exp, block_table, prefix_len, k_tree,
+                              v_tree, kt_exp, vt_exp, cu_nodes, anc, max_nodes: int,
+                              max_prefix: int, scale: float | None = None, *, out=None, lse=None,
+                              want_lse: bool = True, workspace=None, err=None, stream=None):
+    """Tree attention on the FP8 matrix cores: q bf16 (quantized per row inside);
+    k_cache/v_cache [num_blocks, hkv, 64, 128] and k_tree/v_tree [total, hkv, 128] uint8
+    E4M3 with k_exp/v_exp [num_blocks, hkv, 64] and kt_exp/vt_exp [total, hkv] uint8 E8M0
+    row exponents (tree_quantize_rows_e4m3 writes this format).  Returns (out, lse, err)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, torch.uint8, 4)
+    for name, t in (("k_exp", k_exp), ("v_exp", v_exp), ("k_tree", k_tree), ("v_tree", v_tree)):
+        _need(t, name, torch.uint8, 3)
+    for name, t in (("kt_exp", kt_exp), ("vt_exp", vt_exp)):
+        _need(t, name, torch.uint8, 2)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(prefix_len, "prefix_len", torch.int32, 1)
+    _need(cu_nodes, "cu_nodes", torch.int32, 1)
+    _need(anc, "anc", torch.int64, 2)
+    total, hq, d = q.shape
+    num_blocks, hkv, blk, d2 = k_cache.shape
+    if d != 128 or blk != TV_BLOCK or d2 != 128 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks, hkv, 64, 128] and head_dim 128")
+    if tuple(k_exp.shape) != (num_blocks, hkv, TV_BLOCK) or tuple(v_exp.shape) != tuple(k_exp.shape):
+        raise ValueError("k_exp/v_exp must be [num_blocks, hkv, 64]")
+    if tuple(k_tree.shape) != (total, hkv, d) or tuple(v_tree.shape) != (total, hkv, d):
+        raise ValueError("k_tree/v_tree must be [total_nodes, hkv, 128]")
+    if tuple(kt_exp.shape) != (total, hkv) or tuple(vt_exp.shape) != (total, hkv):
+        raise ValueError("kt_exp/vt_exp must be [total_nodes, hkv]")
+    batch = cu_nodes.numel() - 1
+    if block_table.shape[0] != batch or prefix_len.numel() != batch or anc.shape[0] != total:
+        raise ValueError("block_table / prefix_len per sequence, anc per node")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((total, hq), dtype=torch.float32, device=q.device)
+    need = tree_verify_attention_fp8_workspace_size(batch, total, max_nodes, max_prefix, hq, hkv)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    err = _err_word(err, q.device)
+    _check("tree_verify_attention_fp8",
+           lib.tree_verify_attention_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_exp),
+                                         _ptr(v_exp), num_blocks, _ptr(block_table),
+                                         block_table.shape[1], _ptr(prefix_len), _ptr(k_tree),
+                                         _ptr(v_tree), _ptr(kt_exp), _ptr(vt_exp), _ptr(cu_nodes),
+                                         _ptr(anc), anc.shape[1], batch, total, max_nodes,
+                                         max_prefix, hq, hkv, scale, _ptr(out), _ptr(lse),
+                                         _ptr(workspace), ws_bytes, _ptr(err), _stream(stream)))
+    return out, lse, err

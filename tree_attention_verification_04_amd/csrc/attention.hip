@@ -16,7 +16,7 @@
 namespace tv {
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
-                        int head_dim, int dtype, bool fp8_kv) {
+                        int head_dim, int dtype, int kv_format) {
   AttnPlan p{};
   p.mfma = dtype == TV_DTYPE_BF16 && head_dim == 128;
   p.splits = 1;
@@ -47,7 +47,9 @@ AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefi
   p.total_work = base * p.splits;
   // (an FP8 prefix cache goes through the pipelined kernel's register path for long
   // items, through the register-staged kernel for short ones)
-  p.long_items = p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles;
+  // (the FP8 matrix-core format exists in the pipelined kernel only)
+  p.long_items = p.blocks_per_split + ceil_div(max_nodes, 64) >= kLongMinTiles ||
+                 kv_format == kKvMma8;
   // more long work items than compute units, from sequences of different lengths:
   // rank the (sequence, KV head) pairs by cost and start the longest first
   const long pairs = static_cast<long>(batch) * hkv;
@@ -130,7 +132,7 @@ extern "C" size_t tree_verify_attention_workspace_size(int32_t batch, int32_t to
                                                        int32_t dtype) {
   if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return 0;
   return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype,
-                            false)
+                            tv::kKvBf16)
       .workspace;
 }
 
@@ -139,17 +141,27 @@ extern "C" size_t tree_verify_attention_fp8kv_workspace_size(int32_t batch, int3
                                                              int32_t hq, int32_t hkv) {
   if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return 0;
   return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, 128,
-                            TV_DTYPE_BF16, true)
+                            TV_DTYPE_BF16, tv::kKvFp8)
+      .workspace;
+}
+
+extern "C" size_t tree_verify_attention_fp8_workspace_size(int32_t batch, int32_t total_nodes,
+                                                           int32_t max_nodes, int32_t max_prefix,
+                                                           int32_t hq, int32_t hkv) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv != 0) return 0;
+  return tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, 128,
+                            TV_DTYPE_BF16, tv::kKvMma8)
       .workspace;
 }
 
 namespace {
 
-// Shared body of the bf16/fp32 and the FP8-cache entry points (fp8 false: the
-// cache has the dtype of q and no scales).
-int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cache,
+// Shared body of the bf16/fp32 and the two FP8-cache entry points (kv_format: the
+// cache has the dtype of q; E4M3 with fp32 row scales; E4M3 with E8M0 row exponents).
+int verify_attention(const char* fn, int kv_format, const void* q, const void* k_cache,
                      const void* v_cache, const float* k_scale, const float* v_scale,
-                     int32_t num_blocks,
+                     const uint8_t* k_exp, const uint8_t* v_exp, const uint8_t* kt_exp,
+                     const uint8_t* vt_exp, int32_t num_blocks,
                      const int32_t* block_table, int32_t max_blocks, const int32_t* prefix_len,
                      const void* k_tree, const void* v_tree, const int32_t* cu_nodes,
                      const uint64_t* anc_bits, int32_t words, int32_t batch, int32_t total_nodes,
@@ -180,8 +192,18 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
     return bad(TV_EINVAL, "null q, tree K/V, anc_bits, out or prefix_len");
   if (max_prefix > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
     return bad(TV_EINVAL, "null paged cache or block table");
-  if (max_prefix > 0 && fp8 && (k_scale == nullptr || v_scale == nullptr))
+  if (max_prefix > 0 && kv_format == tv::kKvFp8 && (k_scale == nullptr || v_scale == nullptr))
     return bad(TV_EINVAL, "null cache scales");
+  if (max_prefix > 0 && kv_format == tv::kKvMma8 && (k_exp == nullptr || v_exp == nullptr))
+    return bad(TV_EINVAL, "null cache exponents");
+  if (kv_format == tv::kKvMma8 && (kt_exp == nullptr || vt_exp == nullptr))
+    return bad(TV_EINVAL, "null tree exponents");
+  if (kv_format == tv::kKvMma8) {  // rows are loaded in 16-byte chunks
+    auto misaligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; };
+    if (misaligned(k_tree) || misaligned(v_tree) ||
+        (max_prefix > 0 && (misaligned(k_cache) || misaligned(v_cache))))
+      return bad(TV_EINVAL, "E4M3 arrays must be 16-byte aligned");
+  }
   if (max_prefix > 0 && num_blocks < 1)
     return bad(TV_EINVAL, "max_prefix > 0 needs num_blocks >= 1");
   if (static_cast<long>(max_blocks) * 64 < max_prefix)
@@ -190,7 +212,8 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
     return bad(TV_EUNSUPPORTED, "too many (node, head) rows");
 
   const tv::AttnPlan plan =
-      tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype, fp8);
+      tv::plan_attention(batch, total_nodes, max_nodes, max_prefix, hq, hkv, head_dim, dtype,
+                         kv_format);
   if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
     return bad(TV_EWORKSPACE, "workspace missing or too small");
 
@@ -204,7 +227,7 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
   a.v_tree = v_tree;
   a.cu_nodes = cu_nodes;
   a.anc = anc_bits;
-  if (fp8) {  // the kernel choice keys on a non-null scale pointer
+  if (kv_format == tv::kKvFp8) {  // the kernel choice keys on a non-null scale pointer
     a.k_scale = k_scale;
     a.v_scale = v_scale;
   }
@@ -239,6 +262,14 @@ int verify_attention(const char* fn, bool fp8, const void* q, const void* k_cach
   if (plan.persistent) a.queue = reinterpret_cast<int*>(wsb) + tv::kQueueWord;
   if (plan.merge_in_kernel) a.tickets = reinterpret_cast<int*>(wsb) + tv::kTicketWord;
   auto s = static_cast<hipStream_t>(stream);
+  if (kv_format == tv::kKvMma8) {  // the kernel keys on kt8
+    a.k_exp = k_exp;
+    a.v_exp = v_exp;
+    a.kt8 = static_cast<const uint8_t*>(k_tree);
+    a.vt8 = static_cast<const uint8_t*>(v_tree);
+    a.kt_e = kt_exp;
+    a.vt_e = vt_exp;
+  }
   if (!plan.mfma) return tv::launch_attn_vec(a, head_dim, dtype, s);
   if (plan.ordered) {
     int* order = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.order_off);
@@ -262,8 +293,8 @@ extern "C" int tree_verify_attention(const void* q, const void* k_cache, const v
                                      float softmax_scale, void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, int32_t* err, void* stream) {
   tv::clear_error();
-  return verify_attention("tree_verify_attention", false, q, k_cache, v_cache, nullptr, nullptr,
-                          num_blocks, block_table, max_blocks, prefix_len, k_tree, v_tree,
+  return verify_attention("tree_verify_attention", tv::kKvBf16, q, k_cache, v_cache, nullptr,
+                          nullptr, nullptr, nullptr, nullptr, nullptr, num_blocks, block_table, max_blocks, prefix_len, k_tree, v_tree,
                           cu_nodes, anc_bits, words, batch, total_nodes, max_nodes, max_prefix, hq,
                           hkv, head_dim, dtype, softmax_scale, out, lse, workspace,
                           workspace_bytes, err, stream);
@@ -277,8 +308,24 @@ extern "C" int tree_verify_attention_fp8kv(
     int32_t max_nodes, int32_t max_prefix, int32_t hq, int32_t hkv, float softmax_scale,
     void* out, float* lse, void* workspace, size_t workspace_bytes, int32_t* err, void* stream) {
   tv::clear_error();
-  return verify_attention("tree_verify_attention_fp8kv", true, q, k_cache, v_cache, k_scale,
-                          v_scale, num_blocks, block_table,
+  return verify_attention("tree_verify_attention_fp8kv", tv::kKvFp8, q, k_cache, v_cache, k_scale,
+                          v_scale, nullptr, nullptr, nullptr, nullptr, num_blocks, block_table,
+                          max_blocks, prefix_len, k_tree, v_tree, cu_nodes, anc_bits, words, batch,
+                          total_nodes, max_nodes, max_prefix, hq, hkv, 128, TV_DTYPE_BF16,
+                          softmax_scale, out, lse, workspace, workspace_bytes, err, stream);
+}
+
+extern "C" int tree_verify_attention_fp8(
+    const void* q, const uint8_t* k_cache, const uint8_t* v_cache, const uint8_t* k_exp,
+    const uint8_t* v_exp, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+    const int32_t* prefix_len, const uint8_t* k_tree, const uint8_t* v_tree, const uint8_t* kt_exp,
+    const uint8_t* vt_exp, const int32_t* cu_nodes, const uint64_t* anc_bits, int32_t words,
+    int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix, int32_t hq,
+    int32_t hkv, float softmax_scale, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, int32_t* err, void* stream) {
+  tv::clear_error();
+  return verify_attention("tree_verify_attention_fp8", tv::kKvMma8, q, k_cache, v_cache, nullptr,
+                          nullptr, k_exp, v_exp, kt_exp, vt_exp, num_blocks, block_table,
                           max_blocks, prefix_len, k_tree, v_tree, cu_nodes, anc_bits, words, batch,
                           total_nodes, max_nodes, max_prefix, hq, hkv, 128, TV_DTYPE_BF16,
                           softmax_scale, out, lse, workspace, workspace_bytes, err, stream);

@@ -35,6 +35,14 @@ struct AttnArgs {
   int tail_pieces, tail_whole, tail_items;
   int die_slots;            // queue slots per die (persistent launch)
   float scale;              // softmax scale (natural-exp units)
+  // FP8 matrix-core mode (null otherwise): the paged cache's E8M0 row exponents and
+  // the tree's K/V in the same format (E4M3 codes, E8M0 exponents)
+  const uint8_t* k_exp;     // [num_blocks, hkv, 64]
+  const uint8_t* v_exp;
+  const uint8_t* kt8;       // [total_nodes, hkv, 128]
+  const uint8_t* vt8;
+  const uint8_t* kt_e;      // [total_nodes, hkv]
+  const uint8_t* vt_e;
 };
 
 // Kernel arguments sit in memory, and each first use of a field would otherwise
@@ -91,6 +99,11 @@ struct AttnPlan {
   size_t part_off, lse_off, order_off;  // workspace offsets
 };
 
+// cache formats of the matrix-core plans
+constexpr int kKvBf16 = 0;    // the dtype of q
+constexpr int kKvFp8 = 1;     // E4M3 with fp32 row scales
+constexpr int kKvMma8 = 2;    // E4M3 with E8M0 row exponents, on the FP8 matrix cores
+
 // Counter words at the start of the workspace (zero between calls).
 constexpr int kCounterBytes = 2048;
 constexpr int kQueueWord = 0;        // [8] queue heads, [8] exit count of a persistent launch
@@ -98,7 +111,7 @@ constexpr int kTicketWord = 16;      // finish tickets from here
 constexpr int kMaxTickets = kCounterBytes / 4 - kTicketWord;
 
 AttnPlan plan_attention(int batch, int total_nodes, int max_nodes, int max_prefix, int hq, int hkv,
-                        int head_dim, int dtype, bool fp8_kv);
+                        int head_dim, int dtype, int kv_format);
 
 int launch_attn_vec(const AttnArgs& a, int head_dim, int dtype, hipStream_t s);
 int launch_attn_mfma(const AttnArgs& a, hipStream_t s);

@@ -34,6 +34,7 @@
 // probabilities that enter the P.V product).
 #include <mutex>
 
+#include "fp8_quant.h"
 #include "mfma_tile.h"
 
 namespace tv {
@@ -50,6 +51,28 @@ constexpr int kAncSlotBytes = kMfmaRowsPerWG * 8;  // per wavefront: 32 low, 32 
 constexpr int kAncOffL = kVOff + kRing * kTileBytes;
 constexpr int kMaskOff = kAncOffL + kRing * kAncSlotBytes;
 constexpr int kSmemL = kMaskOff + 64;
+// LDS of the FP8 matrix-core mode: E4M3 K ring, bf16 V ring, E4M3 V staging ring,
+// ancestor ring, exponent ring (per tile: K exponents in dwords 0-63, V in 64-127)
+constexpr int kTile8Bytes = kKT * kD;  // 64 keys x 128 E4M3 bytes
+constexpr int kExpSlotBytes = 512;
+constexpr int kVOff8 = kRing * kTile8Bytes;
+constexpr int kV8Off = kVOff8 + kRing * kTileBytes;
+constexpr int kAncOff8 = kV8Off + kRing * kTile8Bytes;
+constexpr int kExpOff = kAncOff8 + kRing * kAncSlotBytes;
+constexpr int kMaskOff8 = kExpOff + kRing * kExpSlotBytes;
+constexpr int kSmem8 = kMaskOff8 + 64;
+static_assert(kSmem8 <= 160 * 1024, "LDS of the FP8 matrix-core mode");
+// modes of the pipelined kernel
+constexpr int kModeBf16 = 0;   // bf16 cache, tiles by direct loads
+constexpr int kModeFp8 = 1;    // E4M3 cache with fp32 row scales, tiles through registers
+constexpr int kModeMma8 = 2;   // E4M3 Q, K, V with power-of-two row scales, FP8 matrix cores
+template <int kMode>
+struct Layout {
+  static constexpr int v_off = kMode == kModeMma8 ? kVOff8 : kVOff;
+  static constexpr int anc_off = kMode == kModeMma8 ? kAncOff8 : kAncOffL;
+  static constexpr int mask_off = kMode == kModeMma8 ? kMaskOff8 : kMaskOff;
+  static constexpr int smem = kMode == kModeMma8 ? kSmem8 : kSmemL;
+};
 constexpr int kLoadsPerIter = 5;      // per lane: 2 K chunks, 1 ancestor dword, 2 V chunks
 // A computing wavefront issues the K group of an iteration's loads after the first
 // score MFMA of the iteration's first half-step and the V group after the first of
@@ -60,6 +83,7 @@ constexpr int kIssueAt = 0;
 static_assert(kWavesL * 32 == kMfmaRowsPerWG, "256 rows per workgroup");
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   typedef __attribute__((address_space(3))) const char lds_char_t;
@@ -113,6 +137,63 @@ __device__ __forceinline__ void issue_v_loads(const void* vb, uint32_t vo0, uint
       : "memory");
 }
 
+// The FP8 matrix-core mode's K group: one 16-byte chunk of the E4M3 K tile (LDS
+// lds_k + 16 l), the K and V exponent bytes of key l (byte-wide direct loads: lane l's
+// byte lands zero-extended in dword l, K at lds_e, V at lds_e + 256), the ancestor
+// dword.  Four loads per lane.  (Dword loads of a prefix tile's 64 contiguous
+// exponents, read back a byte per key, made the calls slower.)
+__device__ __forceinline__ void issue_k8_loads(const void* kb, uint32_t ko, uint32_t lds_k,
+                                               const void* keb, const void* veb, uint32_t eo,
+                                               uint32_t lds_e, const void* ab, uint32_t ao,
+                                               uint32_t lds_a) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[lk]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[k0], %[kb]\n\t"
+      "s_mov_b32 m0, %[le]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_ubyte %[e0], %[keb]\n\t"
+      "s_add_u32 m0, m0, 0x100\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_ubyte %[e0], %[veb]\n\t"
+      "s_mov_b32 m0, %[la]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %[a0], %[ab]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [k0] "v"(ko), [kb] "s"(kb), [lk] "s"(lds_k), [e0] "v"(eo), [keb] "s"(keb),
+        [veb] "s"(veb), [le] "s"(lds_e), [a0] "v"(ao), [ab] "s"(ab), [la] "s"(lds_a)
+      : "memory");
+}
+
+// ... and its V group: one 16-byte chunk of the E4M3 V tile into the staging ring.
+__device__ __forceinline__ void issue_v8_load(const void* vb, uint32_t vo, uint32_t lds_v) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[lv]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[v0], %[vb]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [v0] "v"(vo), [vb] "s"(vb), [lv] "s"(lds_v)
+      : "memory");
+}
+
+// 8 E4M3 bytes (w0, w1) times the power of two `scale` to 8 bf16: the conversion
+// instruction applies the exponent of its fp32 scale operand, exactly
+__device__ __forceinline__ uint4 fp8x8_to_bf16_pow2(uint32_t w0, uint32_t w1, float scale) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+  const bf16x2v b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+  const bf16x2v c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+  const bf16x2v d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
 // The ancestor dword of this lane's row alone (the FP8 pipeline's one direct load per
 // iteration; its tiles come through registers).
 __device__ __forceinline__ void issue_anc_load(const void* ab, uint32_t ao, uint32_t lds_a) {
@@ -139,6 +220,15 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// a pointer that is the same in every lane, moved to scalar registers
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // pin a value: the computation that produces it stays before this point
 __device__ __forceinline__ void pin(uint32_t v) { asm volatile("" : : "v"(v)); }
 __device__ __forceinline__ void pin(float v) { asm volatile("" : : "v"(v)); }
@@ -157,10 +247,13 @@ struct Slot {
 // dequantized on the way, byte x scale rounded to bf16; a tree tile copied), so the
 // rest of the kernel is the bf16 one.  Each iteration still issues five loads per lane
 // (four register loads and the ancestor dword), so the same wait holds.
-template <bool kFp8>
+template <int kMode>
 __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, const int k_slot) {
+  constexpr bool kFp8 = kMode == kModeFp8;
+  constexpr bool kMma8 = kMode == kModeMma8;
+  using L = Layout<kMode>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + kMaskOff);
+  uint32_t* s_tree_mask = reinterpret_cast<uint32_t*>(smem + L::mask_off);
 
   // ---- work item.  Pair rank r (in pair_order, longest first, when given) goes to
   // die r % 8; the m = row_tiles * splits work items of a pair get consecutive
@@ -230,7 +323,16 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
   const long grow = static_cast<long>(n0 + rr / a.group) * a.hq + g * a.group + rr % a.group;
   const bool wave_live = r0 + 32 * wave < rows;
   bf16x8_t q[8];
-  {
+  v8i_t q8[2];         // FP8 matrix-core mode: E4M3 codes of d = 64 m + 32 half + 0..31
+  int q_exp = 127;     // and the row's E8M0 exponent
+  uint4 qw[8];         // FP8 matrix-core mode: the bf16 row, quantized after the tile loads
+  if constexpr (kMma8) {
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q) + grow * kD + 32 * half;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      qw[j] = row_ok ? *reinterpret_cast<const uint4*>(qr + 64 * (j >> 2) + 8 * (j & 3))
+                     : make_uint4(0, 0, 0, 0);
+  } else {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + grow * kD + half * 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
@@ -274,7 +376,7 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       static_cast<uint32_t>(min((r0 + rl) / a.group, count - 1) * a.words * 8 + 4 * half);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_kv = lds_addr(smem) + wave_u * 1024;
-  const uint32_t lds_anc = lds_addr(smem) + kAncOffL + wave_u * 256;
+  const uint32_t lds_anc = lds_addr(smem) + L::anc_off + wave_u * 256;
 
   // source of tile it (clamped to the last tile)
   struct Src {
@@ -327,6 +429,89 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       __attribute__((always_inline)) {
     issue_k(sk, slot_k);
     issue_v(sv, slot_v);
+  };
+
+  // ---- FP8 matrix-core mode: tiles of E4M3 rows (64 keys x 128 bytes), all by direct
+  // loads, K and V of a tile in the same iteration.  Chunk p = 64 w + l of a tile (16
+  // bytes) is lane l of wave w: K row p / 8 at stored position p % 8, which holds the
+  // row's global chunk (p % 8) ^ ((row / 2) % 8) (so that the 32 lanes reading one
+  // chunk position of 32 rows spread over the banks); V row p / 8, chunk p % 8 as is
+  // (converted in place order).  Exponent lane l: key l.  Rows past a partial tile
+  // repeat its last row.
+  struct Src8 {
+    const char* k;
+    const char* v;
+    const uint8_t* ke;
+    const uint8_t* ve;
+    uint32_t ko, vo, eo, anc;
+  };
+  const int p8 = 64 * wave + lane;
+  const int row8 = p8 >> 3;
+  const int kch8 = (p8 & 7) ^ ((row8 >> 1) & 7);
+  const int vch8 = p8 & 7;
+  auto tile_src8 = [&](int it) __attribute__((always_inline)) -> Src8 {
+    int kind, base;
+    tile_kind(min(it, n_tiles - 1), kind, base);
+    Src8 s8;
+    int stride, estride, nvalid;
+    if (kind == 0) {
+      s8.anc = anc_lane;
+      const int blk = bt_row[base / kKT];
+      nvalid = min(kKT, plen - base);
+      long row0 = static_cast<long>(g) * kKT;  // block 0 stands in for a bad id
+      if (blk < 0 || blk >= a.num_blocks) {
+        if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
+        nvalid = 1;
+      } else {
+        row0 = (static_cast<long>(blk) * a.hkv + g) * kKT;
+      }
+      s8.k = kc + row0 * kD;
+      s8.v = vc + row0 * kD;
+      s8.ke = a.k_exp + row0;
+      s8.ve = a.v_exp + row0;
+      stride = kD;
+      estride = 1;
+    } else {
+      s8.anc = anc_lane + base * 8;
+      nvalid = min(64, count - base * 64);
+      const long row0 = static_cast<long>(n0 + base * 64) * a.hkv + g;
+      s8.k = reinterpret_cast<const char*>(a.kt8) + row0 * kD;
+      s8.v = reinterpret_cast<const char*>(a.vt8) + row0 * kD;
+      s8.ke = a.kt_e + row0;
+      s8.ve = a.vt_e + row0;
+      stride = a.hkv * kD;
+      estride = a.hkv;
+    }
+    s8.k = uniform_ptr(s8.k);  // (uniform: block id, sequence and head are)
+    s8.v = uniform_ptr(s8.v);
+    s8.ke = uniform_ptr(s8.ke);
+    s8.ve = uniform_ptr(s8.ve);
+    s8.ko = min(row8, nvalid - 1) * stride + 16 * kch8;
+    s8.vo = min(row8, nvalid - 1) * stride + 16 * vch8;
+    s8.eo = min(lane, nvalid - 1) * estride;
+    return s8;
+  };
+  const uint32_t lds_k8 = lds_addr(smem) + wave_u * 1024;
+  const uint32_t lds_v8 = lds_addr(smem) + kV8Off + wave_u * 1024;
+  const uint32_t lds_e8 = lds_addr(smem) + kExpOff;
+  auto issue_k8 = [&](const Src8& t, int slot) __attribute__((always_inline)) {
+    issue_k8_loads(t.k, t.ko, lds_k8 + slot * kTile8Bytes, t.ke, t.ve, t.eo,
+                   lds_e8 + slot * kExpSlotBytes, anc_base, t.anc, lds_anc + slot * kAncSlotBytes);
+  };
+  auto issue_v8 = [&](const Src8& t, int slot) __attribute__((always_inline)) {
+    issue_v8_load(t.v, t.vo, lds_v8 + slot * kTile8Bytes);
+  };
+  // V tile of staging slot `slot` to bf16 in the V ring's slot `slot`: thread t takes
+  // key t / 8, bytes 16 (t % 8) .. +15, times the key's power-of-two scale
+  auto convert_v = [&](int slot) __attribute__((always_inline)) {
+    const int key = tid >> 3, c8 = tid & 7;
+    const uint4 w = *reinterpret_cast<const uint4*>(smem + kV8Off + slot * kTile8Bytes + 16 * tid);
+    const uint32_t e =
+        *reinterpret_cast<const uint32_t*>(smem + kExpOff + slot * kExpSlotBytes + 256 + 4 * key);
+    const float sc = __uint_as_float(e << 23);
+    char* vst = smem + kVOff8 + slot * kTileBytes;
+    *reinterpret_cast<uint4*>(vst + v_off(key, 2 * c8)) = fp8x8_to_bf16_pow2(w.x, w.y, sc);
+    *reinterpret_cast<uint4*>(vst + v_off(key, 2 * c8 + 1)) = fp8x8_to_bf16_pow2(w.z, w.w, sc);
   };
 
   // ---- FP8 pipeline: a tile's registers.  FP8 prefix tile: thread t holds the 16
@@ -413,6 +598,16 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       issue_anc(2, 2);
       load_regs(2, rx);
       load_regs(3, ry);
+    } else if constexpr (kMma8) {
+      // K, exponents, ancestor words and V of tiles 0, 1 and 2 (V(0) is converted
+      // before the first iteration, V(t + 1) in iteration t)
+      const Src8 t0 = tile_src8(0), t1 = tile_src8(1), t2 = tile_src8(2);
+      issue_k8(t0, 0);
+      issue_v8(t0, 0);
+      issue_k8(t1, 1);
+      issue_v8(t1, 1);
+      issue_k8(t2, 2);
+      issue_v8(t2, 2);
     } else {
       sv = tile_src(2);
       const Src t0 = tile_src(0), t1 = tile_src(1);
@@ -420,7 +615,7 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       issue(t1, 1, t0, 0);
       issue(sv, 2, t1, 1);
     }
-    uint4* vz = reinterpret_cast<uint4*>(smem + kVOff + 3 * kTileBytes);
+    uint4* vz = reinterpret_cast<uint4*>(smem + L::v_off + 3 * kTileBytes);
 #pragma unroll
     for (int j = 0; j < kTileBytes / 16 / kTL; ++j) vz[tid + kTL * j] = make_uint4(0, 0, 0, 0);
   };
@@ -455,12 +650,53 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     const char* kaddr[8];  // K operand of score step r in slot 0, keys 0-31
 #pragma unroll
     for (int r = 0; r < 8; ++r) kaddr[r] = smem + krow0 * 256 + (((2 * r + half) ^ k_xor) << 4);
+    if constexpr (kMma8) {
+      // q's row quantized with the rule of the row quantizer (after the first tile
+      // loads are on their way): its maximum from both halves (lanes col and col + 32
+      // hold the row), bf16 magnitudes compared as integers
+      uint32_t mb = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t ww[4] = {qw[j].x, qw[j].y, qw[j].z, qw[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mb = max(mb, max(ww[e] & 0x7fffu, (ww[e] >> 16) & 0x7fffu));
+      }
+      const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+      mb = max(sw[0], sw[1]);
+      const int sh = e8m0_shift(__uint_as_float(mb << 16));
+      q_exp = sh + 127;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t ww[4] = {qw[j].x, qw[j].y, qw[j].z, qw[j].w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = ldexpf(__uint_as_float(ww[e] << 16), -sh);
+          f[2 * e + 1] = ldexpf(__uint_as_float(ww[e] & 0xffff0000u), -sh);
+        }
+        uint32_t c0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        c0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], c0, true);
+        uint32_t c1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        c1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], c1, true);
+        q8[j >> 2][2 * (j & 3)] = static_cast<int>(c0);
+        q8[j >> 2][2 * (j & 3) + 1] = static_cast<int>(c1);
+      }
+    }
+    // FP8 matrix-core mode: the E4M3 K operand of MFMA m (d = 64 m + 32 half + 0..31,
+    // two chunks) in slot 0, keys 0-31, and this lane's key exponent
+    const char* kaddr8[2][2];
+    const int f8 = (krow0 >> 1) & 7;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) kaddr8[m][j] = smem + krow0 * kD + (((4 * m + 2 * half + j) ^ f8) << 4);
+    const char* keaddr = smem + kExpOff + 4 * krow0;
     const int grp = lane >> 4, jg = lane & 15, hh = grp >> 1;
     const int low = 2 * (grp & 1) + ((jg & 3) >> 1);
     const char* vaddr[4];  // V^T operand of d-tile dt in slot 0, keys 0-15
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      vaddr[dt] = smem + kVOff + (8 * hh + (jg >> 2)) * 256 +
+      vaddr[dt] = smem + L::v_off + (8 * hh + (jg >> 2)) * 256 +
                   ((((dt ^ (jg >> 2)) << 2) + low) << 4) + 8 * (jg & 1);
 
     // visibility of the 32 keys this lane holds in a tile, compressed so that bit
@@ -476,7 +712,7 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         lo = static_cast<uint32_t>(pvis);
         hi = static_cast<uint32_t>(pvis >> 32);
       } else {
-        const uint32_t* s = reinterpret_cast<const uint32_t*>(smem + kAncOffL + slot * kAncSlotBytes);
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(smem + L::anc_off + slot * kAncSlotBytes);
         lo = row_ok ? s[64 * wave + col] : 0u;
         hi = row_ok ? s[64 * wave + 32 + col] : 0u;
       }
@@ -523,11 +759,23 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       mc = mr * c2;
 
       uint4 kr[8];
+      uint4 kr8[2][2];
+      uint32_t ke = 127u;
       bf16x4_t vr[8][2];
       constexpr int kOrder[16] = {0, 1, 8, 2, 9, 3, 10, 4, 11, 5, 12, 6, 13, 7, 14, 15};
       auto read = [&](int r) __attribute__((always_inline)) {  // operand of MFMA r
         if (r < 8) {
-          kr[r] = *reinterpret_cast<const uint4*>(kaddr[r] + ks * kTileBytes + hn * 32 * 256);
+          if constexpr (kMma8) {
+            if ((r & 3) == 0) {
+              const int m = r >> 2;
+              const int off = ks * kTile8Bytes + hn * 32 * kD;
+              kr8[m][0] = *reinterpret_cast<const uint4*>(kaddr8[m][0] + off);
+              kr8[m][1] = *reinterpret_cast<const uint4*>(kaddr8[m][1] + off);
+              if (m == 0) ke = *reinterpret_cast<const uint32_t*>(keaddr + ks * kExpSlotBytes + hn * 128);
+            }
+          } else {
+            kr[r] = *reinterpret_cast<const uint4*>(kaddr[r] + ks * kTileBytes + hn * 32 * 256);
+          }
         } else {
           const int qq = r - 8;
           const char* p = vaddr[qq & 3] + vs * kTileBytes + (32 * hp + 16 * (qq >> 2)) * 256;
@@ -537,8 +785,20 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       };
       auto mfma = [&](int r) __attribute__((always_inline)) {
         if (r < 8) {
-          n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[r]), q[r],
-                                                      r == 0 ? f32x16_t{} : n, 0, 0, 0);
+          if constexpr (kMma8) {
+            if ((r & 3) == 0) {  // scores over d = 64 m .. 64 m + 63, scales applied inside
+              const int m = r >> 2;
+              const v8i_t a8 = {static_cast<int>(kr8[m][0].x), static_cast<int>(kr8[m][0].y),
+                                static_cast<int>(kr8[m][0].z), static_cast<int>(kr8[m][0].w),
+                                static_cast<int>(kr8[m][1].x), static_cast<int>(kr8[m][1].y),
+                                static_cast<int>(kr8[m][1].z), static_cast<int>(kr8[m][1].w)};
+              n = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  a8, q8[m], m == 0 ? f32x16_t{} : n, 0, 0, 0, static_cast<int>(ke), 0, q_exp);
+            }
+          } else {
+            n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[r]), q[r],
+                                                        r == 0 ? f32x16_t{} : n, 0, 0, 0);
+          }
         } else {
           const int qq = r - 8, jj = qq >> 2, dt = qq & 3;
           const bf16x8_t vf = {vr[qq][0][0], vr[qq][0][1], vr[qq][0][2], vr[qq][0][3],
@@ -604,14 +864,25 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         issue_anc(i + 3, (S + 3) % kRing);
         load_regs(i + 4, r);
       }
+      if constexpr (kMma8) convert_v((S + 1) % kRing);  // V(i + 1), landed last iteration
       Src sk{};
-      if constexpr (!kFp8) sk = tile_src(i + 3);
+      Src8 sk8{};
+      if constexpr (kMma8)
+        sk8 = tile_src8(i + 3);
+      else if constexpr (!kFp8)
+        sk = tile_src(i + 3);
       // the K group of this iteration's loads, then the V group (see kIssueAt)
       const auto hk = [&]() __attribute__((always_inline)) {
-        if constexpr (!kFp8) issue_k(sk, (S + 3) % kRing);
+        if constexpr (kMma8)
+          issue_k8(sk8, (S + 3) % kRing);
+        else if constexpr (!kFp8)
+          issue_k(sk, (S + 3) % kRing);
       };
       const auto hv = [&]() __attribute__((always_inline)) {
-        if constexpr (!kFp8) issue_v(sv, (S + 2) % kRing);
+        if constexpr (kMma8)
+          issue_v8(sk8, (S + 3) % kRing);
+        else if constexpr (!kFp8)
+          issue_v(sv, (S + 2) % kRing);
       };
       if (!wave_live) {
         hk();
@@ -625,18 +896,36 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         // probabilities of tile i half 1, scores of tile i+1 half 0, P.V of tile i half 0
         half_step(s0, (S + 1) % kRing, 0, py, S, 0, s1, px, !full, w >> 16, hv);
       }
-      if constexpr (!kFp8) sv = sk;
+      if constexpr (!kFp8 && !kMma8) sv = sk;
       wait_loads_and_barrier<kLoadsPerIter>();
     };
 
     // prologue (issued above): three groups of loads in the iteration pattern, K(0),
     // K(1) and K(2) with their ancestor words and V(0), V(0), V(1)
     wait_loads_and_barrier<kLoadsPerIter>();
+    if constexpr (kMma8) {  // V(0) to bf16 before the first iteration reads it
+      convert_v(0);
+      __syncthreads();
+    }
     if (wave_live) {  // scores of tile 0 half 0
+      if constexpr (kMma8) {
+        const int ke0 = static_cast<int>(*reinterpret_cast<const uint32_t*>(keaddr));
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(kaddr[r])),
-                                                     q[r], r == 0 ? f32x16_t{} : s0, 0, 0, 0);
+        for (int m = 0; m < 2; ++m) {
+          const uint4 x0 = *reinterpret_cast<const uint4*>(kaddr8[m][0]);
+          const uint4 x1 = *reinterpret_cast<const uint4*>(kaddr8[m][1]);
+          const v8i_t a8 = {static_cast<int>(x0.x), static_cast<int>(x0.y), static_cast<int>(x0.z),
+                            static_cast<int>(x0.w), static_cast<int>(x1.x), static_cast<int>(x1.y),
+                            static_cast<int>(x1.z), static_cast<int>(x1.w)};
+          s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8[m], m == 0 ? f32x16_t{} : s0, 0,
+                                                               0, 0, ke0, 0, q_exp);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(*reinterpret_cast<const uint4*>(kaddr[r])), q[r], r == 0 ? f32x16_t{} : s0, 0, 0, 0);
+      }
     }
     int i = 0;
     for (; i + 4 <= n_tiles; i += 4) {
@@ -698,7 +987,7 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    int* s_last = reinterpret_cast<int*>(smem + kMaskOff + 4);
+    int* s_last = reinterpret_cast<int*>(smem + L::mask_off + 4);
     if (tid == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const bool last = atomicAdd(a.tickets + ticket, 1) == n_pieces - 1;
@@ -768,12 +1057,12 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
 }
 
 // Work items as run_work_items hands them out (kQueued: persistent, from the queues).
-template <bool kQueued, bool kFp8>
+template <bool kQueued, int kMode>
 __global__ void __launch_bounds__(kTL, 2) k_attn_long(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  run_work_items<kQueued>(a, reinterpret_cast<int*>(smem + kMaskOff + 8),
+  run_work_items<kQueued>(a, reinterpret_cast<int*>(smem + Layout<kMode>::mask_off + 8),
                  [](const AttnArgs& args, int die, int k_slot) __attribute__((always_inline)) {
-                   long_item<kFp8>(args, die, k_slot);
+                   long_item<kMode>(args, die, k_slot);
                  });
 }
 
@@ -786,27 +1075,38 @@ void set_attn_long_attributes() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 32) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
   if (done & (1u << dev)) return;
-  const void* fns[4] = {reinterpret_cast<const void*>(&k_attn_long<false, false>),
-                          reinterpret_cast<const void*>(&k_attn_long<true, false>),
-                          reinterpret_cast<const void*>(&k_attn_long<false, true>),
-                          reinterpret_cast<const void*>(&k_attn_long<true, true>)};
-  for (const void* f : fns)
-    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemL);
+  const void* fns[6] = {reinterpret_cast<const void*>(&k_attn_long<false, kModeBf16>),
+                        reinterpret_cast<const void*>(&k_attn_long<true, kModeBf16>),
+                        reinterpret_cast<const void*>(&k_attn_long<false, kModeFp8>),
+                        reinterpret_cast<const void*>(&k_attn_long<true, kModeFp8>),
+                        reinterpret_cast<const void*>(&k_attn_long<false, kModeMma8>),
+                        reinterpret_cast<const void*>(&k_attn_long<true, kModeMma8>)};
+  const int bytes[6] = {kSmemL, kSmemL, kSmemL, kSmemL, kSmem8, kSmem8};
+  for (int i = 0; i < 6; ++i)
+    (void)hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
   done |= 1u << dev;
 }
 
 int launch_attn_long(const AttnArgs& a, hipStream_t s) {
   set_attn_long_attributes();
-  const bool fp8 = a.k_scale != nullptr, queued = a.queue != nullptr;
+  const bool queued = a.queue != nullptr;
+  const int mode = a.kt8 != nullptr ? kModeMma8 : (a.k_scale != nullptr ? kModeFp8 : kModeBf16);
   const dim3 grid(queued ? kCUs : 8 * ceil_div(a.batch * a.hkv, 8) * a.row_tiles * a.splits);
-  if (queued && fp8)
-    hipLaunchKernelGGL((k_attn_long<true, true>), grid, dim3(kTL), kSmemL, s, a);
-  else if (queued)
-    hipLaunchKernelGGL((k_attn_long<true, false>), grid, dim3(kTL), kSmemL, s, a);
-  else if (fp8)
-    hipLaunchKernelGGL((k_attn_long<false, true>), grid, dim3(kTL), kSmemL, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_long<false, false>), grid, dim3(kTL), kSmemL, s, a);
+  if (mode == kModeMma8) {
+    if (queued)
+      hipLaunchKernelGGL((k_attn_long<true, kModeMma8>), grid, dim3(kTL), kSmem8, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_long<false, kModeMma8>), grid, dim3(kTL), kSmem8, s, a);
+  } else if (mode == kModeFp8) {
+    if (queued)
+      hipLaunchKernelGGL((k_attn_long<true, kModeFp8>), grid, dim3(kTL), kSmemL, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_long<false, kModeFp8>), grid, dim3(kTL), kSmemL, s, a);
+  } else if (queued) {
+    hipLaunchKernelGGL((k_attn_long<true, kModeBf16>), grid, dim3(kTL), kSmemL, s, a);
+  } else {
+    hipLaunchKernelGGL((k_attn_long<false, kModeBf16>), grid, dim3(kTL), kSmemL, s, a);
+  }
   const int st = check_launch("tree_verify_attention/long");
   if (st != TV_OK || a.splits == 1) return st;
   return launch_attn_combine(a, s);

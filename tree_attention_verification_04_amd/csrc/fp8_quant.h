@@ -22,5 +22,8 @@ __device__ __forceinline__ int e8m0_shift(float amax) {
 // codes [rows][128] and exps [rows] from x [rows][128] (bf16 or fp32)
 int launch_quant_rows(const void* x, int dtype, long rows, uint8_t* codes, uint8_t* exps,
                       hipStream_t stream);
+// two row sets of the same size and dtype in one launch (x1 null: the first only)
+int launch_quant_rows2(const void* x0, uint8_t* codes0, uint8_t* exps0, const void* x1,
+                       uint8_t* codes1, uint8_t* exps1, int dtype, long rows, hipStream_t stream);
 
 }  // namespace tv

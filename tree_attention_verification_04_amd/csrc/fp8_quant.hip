@@ -17,10 +17,19 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 
+// Two row sets in one launch (blockIdx.y selects x / codes / exps of set 0 or 1).
+struct QuantSets {
+  const void* x[2];
+  uint8_t* codes[2];
+  uint8_t* exps[2];
+};
+
 template <bool kBf16>
 __global__ void __launch_bounds__(kQuantThreads)
-    k_quant_rows(const void* __restrict__ x, long rows, uint8_t* __restrict__ codes,
-                 uint8_t* __restrict__ exps) {
+    k_quant_rows(QuantSets sets, long rows) {
+  const void* __restrict__ x = sets.x[blockIdx.y];
+  uint8_t* __restrict__ codes = sets.codes[blockIdx.y];
+  uint8_t* __restrict__ exps = sets.exps[blockIdx.y];
   const long t = static_cast<long>(blockIdx.x) * kQuantThreads + threadIdx.x;
   const long row = t >> 4;
   const int part = static_cast<int>(t & 15);
@@ -61,16 +70,21 @@ __global__ void __launch_bounds__(kQuantThreads)
 
 int launch_quant_rows(const void* x, int dtype, long rows, uint8_t* codes, uint8_t* exps,
                       hipStream_t stream) {
+  return launch_quant_rows2(x, codes, exps, nullptr, nullptr, nullptr, dtype, rows, stream);
+}
+
+int launch_quant_rows2(const void* x0, uint8_t* codes0, uint8_t* exps0, const void* x1,
+                       uint8_t* codes1, uint8_t* exps1, int dtype, long rows, hipStream_t stream) {
   if (rows <= 0) return TV_OK;
   const long threads = rows * 16;
   const long blocks = (threads + kQuantThreads - 1) / kQuantThreads;
   if (blocks > 0x7fffffffL) return fail(TV_EUNSUPPORTED, "quantize: too many rows");
+  const QuantSets sets{{x0, x1}, {codes0, codes1}, {exps0, exps1}};
+  const dim3 grid(static_cast<unsigned>(blocks), x1 != nullptr ? 2 : 1);
   if (dtype == TV_DTYPE_BF16)
-    hipLaunchKernelGGL(k_quant_rows<true>, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0,
-                       stream, x, rows, codes, exps);
+    hipLaunchKernelGGL(k_quant_rows<true>, grid, dim3(kQuantThreads), 0, stream, sets, rows);
   else
-    hipLaunchKernelGGL(k_quant_rows<false>, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0,
-                       stream, x, rows, codes, exps);
+    hipLaunchKernelGGL(k_quant_rows<false>, grid, dim3(kQuantThreads), 0, stream, sets, rows);
   return check_launch("quantize rows");
 }
 
