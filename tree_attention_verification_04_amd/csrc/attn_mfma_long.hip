@@ -138,34 +138,48 @@ __device__ __forceinline__ void issue_v_loads(const void* vb, uint32_t vo0, uint
 }
 
 // The FP8 matrix-core mode's K group: one 16-byte chunk of the E4M3 K tile (LDS
-// lds_k + 16 l), the K and V exponent bytes of key l (byte-wide direct loads: lane l's
-// byte lands zero-extended in dword l, K at lds_e, V at lds_e + 256), the ancestor
-// dword.  Four loads per lane.  (Dword loads of a prefix tile's 64 contiguous
-// exponents, read back a byte per key, made the calls slower.)
+// lds_k + 16 l), in wavefront 0 the K exponent byte of key l and in wavefront 1 the V
+// exponent byte (byte-wide direct loads: lane l's byte lands zero-extended in dword
+// l of lds_e), the ancestor dword.  Four loads per lane in wavefronts 0 and 1, three
+// in the others.  (Dword loads of a prefix tile's 64 contiguous exponents, read back
+// a byte per key, made the calls slower.)
+template <bool kExp>
 __device__ __forceinline__ void issue_k8_loads(const void* kb, uint32_t ko, uint32_t lds_k,
-                                               const void* keb, const void* veb, uint32_t eo,
-                                               uint32_t lds_e, const void* ab, uint32_t ao,
-                                               uint32_t lds_a) {
+                                               const void* eb, uint32_t eo, uint32_t lds_e,
+                                               const void* ab, uint32_t ao, uint32_t lds_a) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[lk]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %[k0], %[kb]\n\t"
-      "s_mov_b32 m0, %[le]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_ubyte %[e0], %[keb]\n\t"
-      "s_add_u32 m0, m0, 0x100\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_ubyte %[e0], %[veb]\n\t"
-      "s_mov_b32 m0, %[la]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %[a0], %[ab]\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [k0] "v"(ko), [kb] "s"(kb), [lk] "s"(lds_k), [e0] "v"(eo), [keb] "s"(keb),
-        [veb] "s"(veb), [le] "s"(lds_e), [a0] "v"(ao), [ab] "s"(ab), [la] "s"(lds_a)
-      : "memory");
+  if constexpr (kExp) {
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[lk]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %[k0], %[kb]\n\t"
+        "s_mov_b32 m0, %[le]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_ubyte %[e0], %[eb]\n\t"
+        "s_mov_b32 m0, %[la]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %[a0], %[ab]\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [k0] "v"(ko), [kb] "s"(kb), [lk] "s"(lds_k), [e0] "v"(eo), [eb] "s"(eb),
+          [le] "s"(lds_e), [a0] "v"(ao), [ab] "s"(ab), [la] "s"(lds_a)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[lk]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %[k0], %[kb]\n\t"
+        "s_mov_b32 m0, %[la]\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %[a0], %[ab]\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [k0] "v"(ko), [kb] "s"(kb), [lk] "s"(lds_k), [a0] "v"(ao), [ab] "s"(ab),
+          [la] "s"(lds_a)
+        : "memory");
+  }
 }
 
 // ... and its V group: one 16-byte chunk of the E4M3 V tile into the staging ring.
@@ -495,8 +509,13 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
   const uint32_t lds_v8 = lds_addr(smem) + kV8Off + wave_u * 1024;
   const uint32_t lds_e8 = lds_addr(smem) + kExpOff;
   auto issue_k8 = [&](const Src8& t, int slot) __attribute__((always_inline)) {
-    issue_k8_loads(t.k, t.ko, lds_k8 + slot * kTile8Bytes, t.ke, t.ve, t.eo,
-                   lds_e8 + slot * kExpSlotBytes, anc_base, t.anc, lds_anc + slot * kAncSlotBytes);
+    if (wave_u < 2)
+      issue_k8_loads<true>(t.k, t.ko, lds_k8 + slot * kTile8Bytes, wave_u == 0 ? t.ke : t.ve, t.eo,
+                           lds_e8 + slot * kExpSlotBytes + 256 * wave_u, anc_base, t.anc,
+                           lds_anc + slot * kAncSlotBytes);
+    else
+      issue_k8_loads<false>(t.k, t.ko, lds_k8 + slot * kTile8Bytes, nullptr, 0u, 0u, anc_base, t.anc,
+                            lds_anc + slot * kAncSlotBytes);
   };
   auto issue_v8 = [&](const Src8& t, int slot) __attribute__((always_inline)) {
     issue_v8_load(t.v, t.vo, lds_v8 + slot * kTile8Bytes);
@@ -848,6 +867,19 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       }
     };
 
+    // end of an iteration: all but this iteration's loads done (per wavefront: the FP8
+    // matrix-core mode issues four in wavefronts 0 and 1, three elsewhere), then the
+    // barrier
+    auto wait_iteration = [&]() __attribute__((always_inline)) {
+      if constexpr (kMma8) {
+        if (wave_u < 2)
+          wait_loads_and_barrier<4>();
+        else
+          wait_loads_and_barrier<3>();
+      } else {
+        wait_loads_and_barrier<kLoadsPerIter>();
+      }
+    };
     f32x16_t s0, s1;         // scores of two consecutive halves
     uint32_t px[8], py[8];   // probabilities of two halves
 #pragma unroll
@@ -897,12 +929,12 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         half_step(s0, (S + 1) % kRing, 0, py, S, 0, s1, px, !full, w >> 16, hv);
       }
       if constexpr (!kFp8 && !kMma8) sv = sk;
-      wait_loads_and_barrier<kLoadsPerIter>();
+      wait_iteration();
     };
 
     // prologue (issued above): three groups of loads in the iteration pattern, K(0),
     // K(1) and K(2) with their ancestor words and V(0), V(0), V(1)
-    wait_loads_and_barrier<kLoadsPerIter>();
+    wait_iteration();
     if constexpr (kMma8) {  // V(0) to bf16 before the first iteration reads it
       convert_v(0);
       __syncthreads();
