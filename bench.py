@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix
+MFMA_FP8_PEAK_TFS = 5000.0     # MI355X dense fp8 matrix
 VALU_FP32_PEAK_TFS = 157.3     # MI355X fp32 vector
 
 
@@ -138,7 +139,8 @@ def summarize_pmc(config: int, fetch_csv: str, write_csv: str, command: str) -> 
     sw = COPY_BYTES / (copy_w * 1024.0)
     # one tree_verify_attention launch: its main kernel plus the split merge, the
     # pair-order kernel and the ticket clear when the plan uses them
-    main_keys = ("k_attn_long", "k_attn_mfma", "k_attn_vec")
+    # (the bf16 instances: the FP8 variants' instances carry mode 1 or 2)
+    main_keys = ("k_attn_long<false, 0>", "k_attn_long<true, 0>", "k_attn_mfma", "k_attn_vec")
     attn_f = next((v for v in (pick(f, k) for k in main_keys) if v is not None), 0.0)
     attn_w = next((v for v in (pick(w, k) for k in main_keys) if v is not None), 0.0)
     aux = ("k_attn_combine", "k_attn_order", "k_clear_words")
@@ -292,57 +294,81 @@ def measure_softmax(tv, case, reps: int) -> dict:
                 frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm")
 
 
+def _graph_us(torch, run, reps: int) -> float:
+    run()
+    torch.cuda.synchronize()
+    return graph_time_us(torch, run, reps)
+
+
 def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict | None:
-    """tree_verify_attention_fp8kv on this workload with its K/V cache quantized to E4M3
-    per (block, head, position) row, timed alone like the bf16 attention.  Algorithmic
-    bytes = the bf16 launch's with the prefix at 1 byte per element plus its 4-byte
-    scales.  None for a non-bf16 workload."""
+    """Both FP8 variants on this workload, each timed alone like the bf16 attention.
+
+    tree_verify_attention_fp8: Q, K and V in E4M3 with power-of-two row scales, scores
+    on the FP8 matrix cores.  Its cache and the tree's K/V are quantized by
+    tree_quantize_rows_e4m3 before the timed region (the forward pass that writes an
+    FP8 cache writes them in that format); q stays bf16 and is quantized inside the
+    call.  Algorithmic bytes = the bf16 launch's with every K/V row at 128 + 1 bytes.
+    Roof: HBM for the workloads whose bf16 call is HBM-bound, else the matrix cores at
+    the peak of its mix (half the flops, Q.K, at the FP8 rate, half, P.V, at the bf16
+    rate: 1 / (0.5 / 5000 + 0.5 / 2500) TFLOP/s).
+
+    tree_verify_attention_fp8kv (E4M3 prefix with fp32 row scales, exact q, tiles
+    through registers): its time beside it.  None for a non-bf16 workload."""
     import torch
     import workloads as W
     if case.dtype != W.DT_BF16 or case.d != 128:
         return None
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    k8, ks = W.fp8_cache(case.k_cache, case.dtype)
-    v8, vs = W.fp8_cache(case.v_cache, case.dtype)
-    k8, v8, ks, vs = t(k8), t(v8), t(ks), t(vs)
-    out = torch.empty_like(dev["q"])
-    need = tv.tree_verify_attention_fp8kv_workspace_size(case.batch, case.total_nodes, mn,
-                                                         case.max_prefix, case.hq, case.hkv)
-    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    run = lambda: tv.tree_verify_attention_fp8kv(
-        dev["q"], k8, v8, ks, vs, dev["block_table"], dev["prefix_len"], dev["k_tree"],
+    # matrix-core variant
+    k8, ke = tv.tree_quantize_rows_e4m3(dev["k_cache"])
+    v8, ve = tv.tree_quantize_rows_e4m3(dev["v_cache"])
+    kt8, kte = tv.tree_quantize_rows_e4m3(dev["k_tree"])
+    vt8, vte = tv.tree_quantize_rows_e4m3(dev["v_tree"])
+    out = torch.empty_like(dev["q"])
+    need = tv.tree_verify_attention_fp8_workspace_size(case.batch, case.total_nodes, mn,
+                                                       case.max_prefix, case.hq, case.hkv)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    us = _graph_us(torch, lambda: tv.tree_verify_attention_fp8(
+        dev["q"], k8, v8, ke, ve, dev["block_table"], dev["prefix_len"], kt8, vt8, kte, vte,
+        dev["cu_nodes"], anc, mn, case.max_prefix, out=out, want_lse=False,
+        workspace=ws if need else None, err=err), reps)
+    # fp32-scale register-path variant
+    k8s, ks = W.fp8_cache(case.k_cache, case.dtype)
+    v8s, vs = W.fp8_cache(case.v_cache, case.dtype)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k8s, v8s, ks, vs = t(k8s), t(v8s), t(ks), t(vs)
+    need_kv = tv.tree_verify_attention_fp8kv_workspace_size(case.batch, case.total_nodes, mn,
+                                                            case.max_prefix, case.hq, case.hkv)
+    ws_kv = torch.zeros(max(need_kv, 1), dtype=torch.uint8, device="cuda")
+    us_kv = _graph_us(torch, lambda: tv.tree_verify_attention_fp8kv(
+        dev["q"], k8s, v8s, ks, vs, dev["block_table"], dev["prefix_len"], dev["k_tree"],
         dev["v_tree"], dev["cu_nodes"], anc, mn, case.max_prefix, out=out, want_lse=False,
-        workspace=ws if need else None, err=err)
-    run()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(reps):
-            run()
-    g.replay()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(5):
-        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_ev.record()
-        g.replay()
-        e_ev.record()
-        torch.cuda.synchronize()
-        times.append(s_ev.elapsed_time(e_ev) / reps)
+        workspace=ws_kv if need_kv else None, err=err), reps)
     if int(err.item()) != 0:
         raise SystemExit(f"fp8 attention: device error word {int(err.item())}")
-    us = float(np.median(times)) * 1e3
-    bf16_bytes, _ = attention_cost(case)
+    bf16_bytes, flops = attention_cost(case)
     prefix_tokens = int(case.prefix_len.sum())
     if case.batch > 1 and np.all(case.block_table == case.block_table[:1]):
         prefix_tokens = int(case.prefix_len.max())
-    bytes_ = bf16_bytes - prefix_tokens * case.hkv * (2 * case.d * 2 - 2 * (case.d + 4))
+    row_save = 2 * (case.d * 2) - 2 * (case.d + 1)  # K and V rows: bf16 -> E4M3 + exponent
+    bytes_ = bf16_bytes - (prefix_tokens + case.total_nodes) * case.hkv * row_save
     gbs = bytes_ / (us * 1e-6) / 1e9
+    t_mem = bf16_bytes / (HBM_PEAK_GBS * 1e9)
+    t_cmp = flops / (MFMA_BF16_PEAK_TFS * 1e12)
+    mix_peak = 1.0 / (0.5 / MFMA_FP8_PEAK_TFS + 0.5 / MFMA_BF16_PEAK_TFS)
+    if t_mem >= t_cmp:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        ach = flops / (us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 2), peak=round(mix_peak, 1), unit="TFLOP/s",
+                    frac=round(ach / mix_peak, 4), hbm_GBps=round(gbs, 1))
     return dict(us_per_launch=round(us, 3), bf16_us_per_launch=round(bf16_us, 3),
-                alg_bytes=int(bytes_), achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm",
-                kernel="matrix-core kernels: E4M3 tiles through registers, dequantized into the bf16 LDS rings")
+                vs_bf16=round(us / bf16_us, 4), alg_bytes=int(bytes_), **roof,
+                kernel="tree_verify_attention_fp8: E4M3 Q.K on the scaled FP8 matrix "
+                       "instructions, V converted to bf16 in LDS",
+                fp32_scale_variant={"entry": "tree_verify_attention_fp8kv",
+                                    "us_per_launch": round(us_kv, 3)})
 
 
 def measure_draft_tree(tv, case, reps: int) -> dict:
