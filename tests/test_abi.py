@@ -275,3 +275,44 @@ def test_step_and_graph_host_checks(lib):
     a.batch, a.total_nodes, a.max_nodes, a.words = 1, 4, 0, 1
     assert lib.tree_verify_step(ctypes.byref(a), None) == tv.TV_EUNSUPPORTED
     assert b"max_nodes" in lib.tree_last_error()
+
+
+def mma8_call(lib, **kw):
+    one = ctypes.c_void_p(16)  # 16-byte aligned, never dereferenced: the checks fail first
+    args = dict(q=one, kc=one, vc=one, ke=one, ve=one, nblocks=4, bt=one, max_blocks=2, plen=one,
+                kt=one, vt=one, kte=one, vte=one, cu=one, anc=one, words=1, batch=1, total=3,
+                max_nodes=3, max_prefix=100, hq=4, hkv=2, scale=0.088, out=one, lse=None, ws=None,
+                ws_bytes=0, err=one, stream=None)
+    args.update(kw)
+    return lib.tree_verify_attention_fp8(*args.values())
+
+
+def test_fp8_matrix_core_attention_host_checks(lib):
+    assert mma8_call(lib, ke=None) == tv.TV_EINVAL               # a prefix needs its exponents
+    assert mma8_call(lib, ve=None) == tv.TV_EINVAL
+    assert b"cache exponents" in lib.tree_last_error()
+    assert mma8_call(lib, kte=None) == tv.TV_EINVAL              # the tree rows always do
+    assert b"tree exponents" in lib.tree_last_error()
+    assert mma8_call(lib, kt=ctypes.c_void_p(24)) == tv.TV_EINVAL  # 16-byte row chunks
+    assert mma8_call(lib, vc=ctypes.c_void_p(40)) == tv.TV_EINVAL
+    assert b"aligned" in lib.tree_last_error()
+    assert mma8_call(lib, hq=3) == tv.TV_EINVAL
+    assert mma8_call(lib, max_prefix=200) == tv.TV_EINVAL
+    assert b"tree_verify_attention_fp8" in lib.tree_last_error()
+    assert mma8_call(lib, batch=0) == tv.TV_OK                  # nothing to do
+    # its plans are the bf16 ones (every work item runs the pipelined kernel)
+    for shape in ((8, 4672, 584, 4096, 32, 8), (4, 1024, 256, 32768, 64, 8), (1, 64, 64, 1088, 32, 32),
+                  (64, 3600, 96, 4096, 32, 8)):
+        assert lib.tree_verify_attention_fp8_workspace_size(*shape) == \
+            lib.tree_verify_attention_workspace_size(*shape, 128, tv.TV_DTYPE_BF16)
+    need = lib.tree_verify_attention_fp8_workspace_size(1, 64, 64, 1088, 32, 32)
+    assert mma8_call(lib, total=64, max_nodes=64, max_prefix=1088, max_blocks=17, hq=32, hkv=32,
+                     ws_bytes=need - 1, ws=ctypes.c_void_p(16)) == tv.TV_EWORKSPACE
+
+
+def test_quantize_rows_host_checks(lib):
+    one = ctypes.c_void_p(16)
+    assert lib.tree_quantize_rows_e4m3(one, tv.TV_DTYPE_BF16, -1, one, one, None) == tv.TV_EINVAL
+    assert lib.tree_quantize_rows_e4m3(one, 7, 4, one, one, None) == tv.TV_EUNSUPPORTED
+    assert lib.tree_quantize_rows_e4m3(None, tv.TV_DTYPE_BF16, 4, one, one, None) == tv.TV_EINVAL
+    assert lib.tree_quantize_rows_e4m3(None, tv.TV_DTYPE_F32, 0, None, None, None) == tv.TV_OK
