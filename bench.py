@@ -300,6 +300,26 @@ def _graph_us(torch, run, reps: int) -> float:
     return graph_time_us(torch, run, reps)
 
 
+def fp8_step_time(torch, tv, case, dev, attention_fp8, mn: int, replays: int) -> float:
+    """The step with the FP8 matrix-core attention in place of the bf16 one (index,
+    attention, acceptance in one captured graph), microseconds per step."""
+    anc = torch.empty((case.total_nodes, (mn + 63) // 64), dtype=torch.int64, device="cuda")
+    depth = torch.empty(case.total_nodes, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_acc = torch.zeros(max(tv.tree_accept_workspace_size(case.batch, case.vocab), 1),
+                         dtype=torch.uint8, device="cuda")
+    outs = {}
+
+    def step():
+        tv.tree_build_index(dev["parent"], dev["cu_nodes"], mn, anc=anc, depth=depth, err=err)
+        attention_fp8(anc)
+        tv.tree_accept(dev["p_target"], dev["p_draft"], dev["token"], dev["u_accept"],
+                       dev["u_resample"], dev["parent"], dev["cu_nodes"], mn, 16, outputs=outs,
+                       workspace=ws_acc, err=err)
+
+    return _graph_us(torch, step, replays)
+
+
 def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict | None:
     """Both FP8 variants on this workload, each timed alone like the bf16 attention.
 
@@ -312,6 +332,7 @@ def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict 
     the peak of its mix (half the flops, Q.K, at the FP8 rate, half, P.V, at the bf16
     rate: 1 / (0.5 / 5000 + 0.5 / 2500) TFLOP/s).
 
+    step_us / step_tokens_per_s: the step with this call in place of the bf16 one.
     tree_verify_attention_fp8kv (E4M3 prefix with fp32 row scales, exact q, tiles
     through registers): its time beside it.  None for a non-bf16 workload."""
     import torch
@@ -328,10 +349,12 @@ def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict 
     need = tv.tree_verify_attention_fp8_workspace_size(case.batch, case.total_nodes, mn,
                                                        case.max_prefix, case.hq, case.hkv)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
-    us = _graph_us(torch, lambda: tv.tree_verify_attention_fp8(
+    attention_fp8 = lambda a_bits: tv.tree_verify_attention_fp8(
         dev["q"], k8, v8, ke, ve, dev["block_table"], dev["prefix_len"], kt8, vt8, kte, vte,
-        dev["cu_nodes"], anc, mn, case.max_prefix, out=out, want_lse=False,
-        workspace=ws if need else None, err=err), reps)
+        dev["cu_nodes"], a_bits, mn, case.max_prefix, out=out, want_lse=False,
+        workspace=ws if need else None, err=err)
+    us = _graph_us(torch, lambda: attention_fp8(anc), reps)
+    step_us = fp8_step_time(torch, tv, case, dev, attention_fp8, mn, 20)
     # fp32-scale register-path variant
     k8s, ks = W.fp8_cache(case.k_cache, case.dtype)
     v8s, vs = W.fp8_cache(case.v_cache, case.dtype)
@@ -365,6 +388,8 @@ def measure_fp8(tv, case, dev, anc, mn: int, bf16_us: float, reps: int) -> dict 
                     frac=round(ach / mix_peak, 4), hbm_GBps=round(gbs, 1))
     return dict(us_per_launch=round(us, 3), bf16_us_per_launch=round(bf16_us, 3),
                 vs_bf16=round(us / bf16_us, 4), alg_bytes=int(bytes_), **roof,
+                step_us=round(step_us, 2),
+                step_tokens_per_s=round(case.total_nodes / (step_us * 1e-6), 1),
                 kernel="tree_verify_attention_fp8: E4M3 Q.K on the scaled FP8 matrix "
                        "instructions, V converted to bf16 in LDS",
                 fp32_scale_variant={"entry": "tree_verify_attention_fp8kv",
