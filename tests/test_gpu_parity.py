@@ -67,6 +67,34 @@ def test_build_index_error_bits(gpu_lib):
     assert int(err.item()) == oracle.ERR_TOO_MANY_NODES
 
 
+@pytest.mark.parametrize("mn", [64, 300])
+def test_build_index_errors_leave_other_sequences(gpu_lib, mn):
+    """A sequence with a bad link or too many nodes (here also past the nodes the
+    launch covers for max_nodes = 300) flags its bit; the other sequences' rows are
+    still exact."""
+    rng = np.random.default_rng(mn)
+    good = [W.tree_random(rng, 40, 5), W.tree_heap(mn), W.tree_chain(mn)]
+    bad = np.array([-1, 0, 3, 1], np.int32)
+    parents = [good[0], W.tree_chain(2 * mn + 7), good[1], bad, good[2]]
+    case = W.make_case("mixed_err", parents, [5, 6, 7, 8, 9], 1, 1, 64, W.DT_F32, 10, 1,
+                       with_probs=False)
+    dev = W.case_to_device(case, probs=False)
+    anc, depth, pos, err = gpu_index(gpu_lib, case, dev, max_nodes=mn)
+    torch.cuda.synchronize()
+    assert int(err.item()) == oracle.ERR_TOO_MANY_NODES | oracle.ERR_BAD_PARENT
+    anc = anc.cpu().numpy().view(np.uint64)
+    depth, pos = depth.cpu().numpy(), pos.cpu().numpy()
+    cu = case.cu_nodes
+    for b in (0, 2, 4):
+        n0, n1 = int(cu[b]), int(cu[b + 1])
+        want_anc, want_depth, want_pos, want_err = oracle.build_index(
+            case.parent[n0:n1], np.array([0, n1 - n0]), mn, case.prefix_len[b:b + 1])
+        assert want_err == 0
+        np.testing.assert_array_equal(anc[n0:n1], want_anc)
+        np.testing.assert_array_equal(depth[n0:n1], want_depth)
+        np.testing.assert_array_equal(pos[n0:n1], want_pos)
+
+
 # ------------------------------------------------------------------ attention
 
 def check_attention(tv, case, tol, nodes=None):

@@ -1151,10 +1151,15 @@ int launch_attn_long(const AttnArgs& a, hipStream_t s) {
 // the same clamped lengths the attention kernel uses.  Key of pair p = cost << 32 |
 // ~p: keys are distinct, so the position of p in the list (larger costs first, equal
 // costs in index order) is the number of keys above its own.  Every workgroup puts
-// all keys in LDS and each of its threads counts for one pair; the counts read the
-// keys at one address per step across the wavefront (a broadcast, no bank
-// conflicts), so the ranks need no sort network and no barrier past the first.
+// all keys in LDS and four adjacent threads count for one pair, thread q of the four
+// over keys q, q + 4, q + 8, ... (so a wavefront reads four adjacent keys per step,
+// in different banks, each a broadcast to 16 lanes), eight loads in flight per
+// thread; the four counts are summed across the lanes.  The ranks need no sort
+// network and no barrier past the first.
 constexpr int kOrderThreads = 256;
+constexpr int kOrderSplit = 4;                                  // threads per pair
+constexpr int kOrderPairsPerWG = kOrderThreads / kOrderSplit;   // pairs ranked per workgroup
+static_assert(64 % kOrderSplit == 0 && kOrderThreads % 64 == 0, "a pair's threads share a wavefront");
 
 __device__ __forceinline__ uint64_t pair_cost_key(const AttnArgs& a, int p) {
   const int b = p / a.hkv;
@@ -1177,24 +1182,34 @@ __global__ void __launch_bounds__(kOrderThreads) k_attn_order(AttnArgs a, int* o
   const int pairs = a.batch * a.hkv;
   for (int p = threadIdx.x; p < pairs; p += kOrderThreads) s_key[p] = pair_cost_key(a, p);
   __syncthreads();
-  const int p = blockIdx.x * kOrderThreads + threadIdx.x;
-  if (p >= pairs) return;
-  const uint64_t mine = s_key[p];
-  int above = 0;
-  int i = 0;
-  for (; i + 4 <= pairs; i += 4) {
-    const uint64_t k0 = s_key[i], k1 = s_key[i + 1], k2 = s_key[i + 2], k3 = s_key[i + 3];
-    above += (k0 > mine) + (k1 > mine) + (k2 > mine) + (k3 > mine);
+  const int q = threadIdx.x % kOrderSplit;
+  const int p = blockIdx.x * kOrderPairsPerWG + threadIdx.x / kOrderSplit;
+  const bool live = p < pairs;  // dead threads still take part in the lane sums below
+  const uint64_t mine = s_key[live ? p : 0];
+  int c0 = 0, c1 = 0;
+  int i = q;
+  for (; i + 7 * kOrderSplit < pairs; i += 8 * kOrderSplit) {
+    uint64_t k[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k[j] = s_key[i + j * kOrderSplit];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      c0 += k[j] > mine;
+      c1 += k[j + 1] > mine;
+    }
   }
-  for (; i < pairs; ++i) above += s_key[i] > mine;
-  order[above] = p;
+  for (; i < pairs; i += kOrderSplit) c0 += s_key[i] > mine;
+  int above = c0 + c1;
+  above += __shfl_xor(above, 1);
+  above += __shfl_xor(above, 2);
+  if (live && q == 0) order[above] = p;
 }
 
 int launch_attn_order(const AttnArgs& a, int* order, hipStream_t s) {
   const int pairs = a.batch * a.hkv;
   if (pairs < 1 || pairs > kMaxOrderedPairs) return TV_EINVAL;
-  hipLaunchKernelGGL(k_attn_order, dim3((pairs + kOrderThreads - 1) / kOrderThreads), dim3(kOrderThreads), 0,
-                     s, a, order);
+  hipLaunchKernelGGL(k_attn_order, dim3((pairs + kOrderPairsPerWG - 1) / kOrderPairsPerWG),
+                     dim3(kOrderThreads), 0, s, a, order);
   return check_launch("tree_verify_attention/order");
 }
 
