@@ -372,7 +372,7 @@ int tree_accept(const float* p_target, const float* p_draft, const int32_t* toke
  * allocation).  Same arguments, outputs, launch and errors as tree_accept, minus
  * the workspace: the chunked launch (vocab > 65536) keeps its ticket words and
  * chunk sums in a fixed scratch array of this library, one copy per GPU (1 MiB +
- * 4 KiB, held until the process ends; its device address is looked up once per
+ * 128 KiB, held until the process ends; its device address is looked up once per
  * device and its ticket words cleared then).  Nothing is allocated per call.
  *
  *   limits       vocab > 65536 needs batch <= 1024 (else TV_EUNSUPPORTED, nothing

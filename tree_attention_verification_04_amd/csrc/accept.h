@@ -8,6 +8,10 @@ namespace tv {
 // Above this vocabulary the launch is chunked and uses the workspace.
 constexpr int kAcceptFusedVocab = 65536;
 
+// Bytes of the finish-ticket words at the start of the workspace (one 128-byte line
+// per sequence, rounded up to 256 bytes).
+size_t accept_ticket_bytes(int batch);
+
 // Argument checks and the one acceptance launch shared by tree_accept and
 // tree_accept_noalloc (workspace: the ticket words and chunk sums of the chunked
 // launch, see tree_accept_workspace_size).

@@ -38,6 +38,9 @@ constexpr int kResidPerThread = kResidChunk / kAcceptThreads;
 constexpr int kFusedVocab = kAcceptFusedVocab;  // up to this vocabulary one workgroup per sequence
 constexpr int kMaxVocab = 1 << 18;
 constexpr int kMaxResidChunks = kMaxVocab / kResidChunk;
+// A sequence's ticket word sits alone in a 128-byte line: the 32 chunk workgroups of
+// 16 sequences took their tickets on one line before (serving-64: 30.6 -> 28.6 us)
+constexpr int kTicketStride = 32;
 static_assert(kResidPerThread % 4 == 0, "whole float4 per thread");
 
 #pragma clang fp contract(off)
@@ -58,7 +61,8 @@ struct AcceptArgs {
   int32_t* resample_node;
   int32_t* resample_token;
   uint8_t* node_ok;
-  int* tickets;             // [batch] finish tickets (chunked launch), zero between calls
+  int* tickets;             // finish tickets (chunked launch), one per kTicketStride ints,
+                            // zero between calls
   uint64_t* part;           // [batch, chunks, 2] chunk sums (chunked launch)
   int32_t* err;
 };
@@ -271,10 +275,33 @@ __device__ void select_token(const AcceptArgs& a, int b, int chunks, const float
   // this thread's weights, loaded once (all loads in flight together) and kept for
   // the walk
   uint64_t wgt[kResidPerThread];
+  const uintptr_t align = reinterpret_cast<uintptr_t>(pt_row + k0) |
+                          (pd_row != nullptr ? reinterpret_cast<uintptr_t>(pd_row + k0) : 0);
+  if (k1 - k0 == kResidPerThread && (align & 15) == 0) {
+    // a whole slice, 16-byte aligned: 16-byte loads (four per row), all in flight
+    float t[kResidPerThread], d[kResidPerThread];
 #pragma unroll
-  for (int e = 0; e < kResidPerThread; ++e) {
-    const int k = k0 + e;
-    wgt[e] = k < k1 ? weight_at(pt_row, pd_row, k, mode) : 0ull;
+    for (int j = 0; j < kResidPerThread / 4; ++j) {
+      const float4 x = reinterpret_cast<const float4*>(pt_row + k0)[j];
+      t[4 * j] = x.x, t[4 * j + 1] = x.y, t[4 * j + 2] = x.z, t[4 * j + 3] = x.w;
+    }
+    if (mode == 0 && pd_row != nullptr) {
+#pragma unroll
+      for (int j = 0; j < kResidPerThread / 4; ++j) {
+        const float4 x = reinterpret_cast<const float4*>(pd_row + k0)[j];
+        d[4 * j] = x.x, d[4 * j + 1] = x.y, d[4 * j + 2] = x.z, d[4 * j + 3] = x.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kResidPerThread; ++e)
+      wgt[e] = mode == 1 ? target_weight(t[e])
+                         : (pd_row != nullptr ? resid_weight(t[e], d[e]) : 0ull);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kResidPerThread; ++e) {
+      const int k = k0 + e;
+      wgt[e] = k < k1 ? weight_at(pt_row, pd_row, k, mode) : 0ull;
+    }
   }
   uint64_t local = 0;
 #pragma unroll
@@ -301,6 +328,7 @@ template <bool kChunked>
 __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int batch, int chunks) {
   __shared__ int16_t s_par[TV_MAX_NODES];
   __shared__ uint8_t s_acc[TV_MAX_NODES];
+  __shared__ float s_ures[TV_MAX_NODES];
   __shared__ int s_bad, s_key, s_child, s_err, s_last;
   const int tid = threadIdx.x;
   // workgroup i runs on die i % 8: the chunks of sequence b all go to die b % 8, so
@@ -333,11 +361,30 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int bat
     }
     return;
   }
+  // parent links, and 1-2. the ratio test per node: u < min(1, pt/pd)  <=>
+  // (double)u * pd < pt for u in [0, 1); every node's resample uniform is kept too,
+  // so that all of a node's loads go out together
+  int my_err = 0;
   for (int i = tid; i < n; i += kAcceptThreads) {
-    const int p = a.parent[n0 + i];
+    const long g = n0 + i;
+    const int p = a.parent[g];
+    const int tok = a.token[g];
+    const float u = a.u_acc[g];
+    s_ures[i] = a.u_res[g];
     s_par[i] = static_cast<int16_t>(p);
     if (p >= i || p < -1) s_bad = 1;
+    bool acc = false;
+    if (tok < 0 || tok >= a.vocab) {
+      my_err |= TV_ERR_TOKEN;
+    } else if (!(u >= 0.0f && u < 1.0f)) {
+      my_err |= TV_ERR_UNIFORM;
+    } else {
+      const long off = g * a.vocab + tok;
+      acc = static_cast<double>(u) * static_cast<double>(a.pd[off]) < static_cast<double>(a.pt[off]);
+    }
+    s_acc[i] = acc ? 1 : 0;
   }
+  if (my_err) atomicOr(&s_err, my_err);
   __syncthreads();
   if (s_bad) {
     if (!writer) return;
@@ -351,28 +398,6 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int bat
     }
     return;
   }
-  // 1-2. ratio test per node: u < min(1, pt/pd)  <=>  (double)u * pd < pt for u in [0, 1)
-  int my_err = 0;
-  for (int i = tid; i < n; i += kAcceptThreads) {
-    const long g = n0 + i;
-    const int tok = a.token[g];
-    bool acc = false;
-    if (tok < 0 || tok >= a.vocab) {
-      my_err |= TV_ERR_TOKEN;
-    } else {
-      const float u = a.u_acc[g];
-      if (!(u >= 0.0f && u < 1.0f)) {
-        my_err |= TV_ERR_UNIFORM;
-      } else {
-        const long off = g * a.vocab + tok;
-        acc = static_cast<double>(u) * static_cast<double>(a.pd[off]) <
-              static_cast<double>(a.pt[off]);
-      }
-    }
-    s_acc[i] = acc ? 1 : 0;
-  }
-  if (my_err) atomicOr(&s_err, my_err);
-  __syncthreads();
   // 3. a node is reached by the walk iff it and all its ancestors passed;
   //    the winner is the reached node of largest depth, smallest index on ties
   for (int i = tid; i < n; i += kAcceptThreads) {
@@ -406,7 +431,7 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int bat
   float u = 0.0f;
   if (c >= 0) {
     snode = c;
-    u = a.u_res[n0 + c];
+    u = s_ures[c];
     if (u >= 0.0f && u < 1.0f) {
       row_t = a.pt + static_cast<long>(n0 + c) * a.vocab;
       row_d = a.pd + static_cast<long>(n0 + c) * a.vocab;
@@ -419,7 +444,7 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int bat
       e |= TV_ERR_ROW;
     } else if (r >= 0) {
       snode = w;
-      u = a.u_res[n0 + w];
+      u = s_ures[w];
       if (u >= 0.0f && u < 1.0f) row_t = a.p_own + static_cast<long>(r) * a.vocab;
       else e |= TV_ERR_UNIFORM;
     }
@@ -458,10 +483,10 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int bat
       const uint64_t o1 =
           __hip_atomic_exchange(slot + 1, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       asm volatile("s_waitcnt vmcnt(0)" : : "v"(o0), "v"(o1) : "memory");  // both returned
-      const bool last = __hip_atomic_fetch_add(a.tickets + b, 1, __ATOMIC_RELAXED,
+      const bool last = __hip_atomic_fetch_add(a.tickets + kTicketStride * b, 1, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT) == chunks - 1;
       // every workgroup of the sequence has taken its ticket: zero it for the next call
-      if (last) __hip_atomic_store(a.tickets + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (last) __hip_atomic_store(a.tickets + kTicketStride * b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = last;
     }
     __syncthreads();
@@ -474,12 +499,18 @@ __global__ void __launch_bounds__(kAcceptThreads) k_accept(AcceptArgs a, int bat
 
 }  // namespace tv
 
-// Workspace: [batch] finish tickets (256-byte aligned), then [batch, chunks, 2] sums.
+// Workspace: [batch] finish tickets, one per 128-byte line (256-byte aligned), then
+// [batch, chunks, 2] sums.
+namespace tv {
+size_t accept_ticket_bytes(int batch) {
+  return (static_cast<size_t>(batch) * kTicketStride * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+}
+}  // namespace tv
+
 extern "C" size_t tree_accept_workspace_size(int32_t batch, int32_t vocab) {
   if (batch <= 0 || vocab <= 0) return 0;
   const size_t chunks = static_cast<size_t>(tv::ceil_div(vocab, tv::kResidChunk));
-  const size_t head = (static_cast<size_t>(batch) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
-  return head + static_cast<size_t>(batch) * chunks * 2 * sizeof(uint64_t);
+  return tv::accept_ticket_bytes(batch) + static_cast<size_t>(batch) * chunks * 2 * sizeof(uint64_t);
 }
 
 namespace tv {
@@ -542,7 +573,7 @@ int accept_launch(const char* fn, const float* p_target, const float* p_draft,
   if (!chunked) {
     hipLaunchKernelGGL(k_accept<false>, dim3(padded), dim3(kAcceptThreads), 0, s, a, batch, 1);
   } else {
-    const size_t head = (static_cast<size_t>(batch) * sizeof(int32_t) + 255) & ~static_cast<size_t>(255);
+    const size_t head = accept_ticket_bytes(batch);
     a.tickets = static_cast<int*>(workspace);
     a.part = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + head);
     hipLaunchKernelGGL(k_accept<true>, dim3(padded * chunks), dim3(kAcceptThreads), 0, s, a,

@@ -11,9 +11,12 @@ namespace tv {
 
 namespace {
 
-// Largest scratch one call may use: tickets for 1024 sequences (4 KiB) plus their
-// chunk sums at the largest vocabulary (1024 x 64 chunks x 16 B = 1 MiB).
-constexpr size_t kScratchBytes = 4096 + (size_t{1} << 20);
+// Largest scratch one call may use: tickets for 1024 sequences (a 128-byte line each,
+// 128 KiB) plus their chunk sums at the largest vocabulary (1024 x 64 chunks x 16 B =
+// 1 MiB).
+constexpr int kMaxSequences = 1024;
+constexpr size_t kTicketBytes = size_t{kMaxSequences} * 128;
+constexpr size_t kScratchBytes = kTicketBytes + (size_t{1} << 20);
 constexpr int kMaxDevices = 64;
 
 // Zero when the code object is loaded; every call leaves its ticket words zero again.
@@ -45,9 +48,11 @@ void* scratch_for_current_device(hipStream_t s, int* status) {
       *status = TV_EHIP;
       return nullptr;
     }
-    // the first 4 KiB hold the ticket words: clear them once, by a kernel (not a
+    // the first 128 KiB hold the ticket words: clear them once, by a kernel (not a
     // memset node) so that a call under graph capture stays valid
-    hipLaunchKernelGGL(k_zero_words, dim3(4), dim3(256), 0, s, static_cast<uint32_t*>(ptr), 1024);
+    constexpr int kWords = static_cast<int>(kTicketBytes / 4);
+    hipLaunchKernelGGL(k_zero_words, dim3(kWords / 256), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ptr), kWords);
     const int st = check_launch("tree_accept_noalloc/clear");
     if (st != TV_OK) {
       *status = st;
@@ -74,7 +79,9 @@ extern "C" int tree_accept_noalloc(const float* p_target, const float* p_draft,
                                    uint8_t* node_ok, int32_t* err, void* stream) {
   tv::clear_error();
   const size_t need = tree_accept_workspace_size(batch, vocab);
-  if (vocab > tv::kAcceptFusedVocab && (need > tv::kScratchBytes || batch > 1024))
+  if (vocab > tv::kAcceptFusedVocab &&
+      (need > tv::kScratchBytes || batch > tv::kMaxSequences ||
+       tv::accept_ticket_bytes(batch) > tv::kTicketBytes))
     return tv::fail(TV_EUNSUPPORTED,
                     "tree_accept_noalloc: batch x vocabulary chunks exceed the fixed scratch "
                     "(at most 1024 sequences; 1 MiB of chunk sums)");
