@@ -492,11 +492,10 @@ __device__ __forceinline__ void mfma_item(const AttnArgs& a, const int die, cons
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
       const int d = 32 * dt + 8 * qd + 4 * half;
-      *reinterpret_cast<float4*>(po + d) =
-          make_float4(acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv, acc[dt][4 * qd + 2] * inv,
-                      acc[dt][4 * qd + 3] * inv);
+      store_stream4(po + d, acc[dt][4 * qd] * inv, acc[dt][4 * qd + 1] * inv,
+                    acc[dt][4 * qd + 2] * inv, acc[dt][4 * qd + 3] * inv);
     }
-  if (half == 0) a.part_lse[static_cast<long>(split) * a.total_rows + grow] = lse;
+  if (half == 0) store_stream(a.part_lse + static_cast<long>(split) * a.total_rows + grow, lse);
 }
 
 // Work items as run_work_items hands them out (kQueued: persistent, from the queues).

@@ -40,6 +40,16 @@ __device__ __forceinline__ int seq_of_node(const int32_t* __restrict__ cu, int b
   return lo;
 }
 
+// Streaming (non-temporal) stores for whole 16-byte pieces that no workgroup of the
+// same launch reads back: they go out as the kernel runs instead of sitting dirty in
+// the die's L2 until the write-back at the end of the launch.
+typedef float stream_f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream4(float* p, float x, float y, float z, float w) {
+  const stream_f32x4_t v = {x, y, z, w};
+  __builtin_nontemporal_store(v, reinterpret_cast<stream_f32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
