@@ -756,7 +756,7 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     // fixed order, S0 S1 P0 S2 P1 .. S7 P6 P7: the score steps of half h+1 (K slot
     // ks, 32-key half hn) into n and the P.V steps of half h-1 (V slot vs, half hp,
     // probabilities pp).  LDS operands are read four MFMAs ahead; between the MFMAs
-    // the vector ALU turns c into probabilities pc, four at a time.  At the end, l
+    // the vector ALU turns c into probabilities pc, one per MFMA.  At the end, l
     // takes the rescale factor and the sum of half h, and so do the accumulators,
     // which then wait for the P.V of half h.
     auto half_step = [&](f32x16_t& n, int ks, int hn, const uint32_t (&pp)[8], int vs, int hp,
@@ -828,19 +828,15 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         }
       };
       float sum = 0.0f;
-      // probabilities of registers 4k .. 4k+3 (each exp result is used two
-      // instructions later or more)
-      auto exp4 = [&](int k) __attribute__((always_inline)) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(c[4 * k + e] * c2 - mc);
-        pc[2 * k] = pack2_bf16(p[0], p[1]);
-        pc[2 * k + 1] = pack2_bf16(p[2], p[3]);
-        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pc[2 * k]), ones, sum, false);
-        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pc[2 * k + 1]), ones, sum,
-                                              false);
-        pin(pc[2 * k]);
-        pin(pc[2 * k + 1]);
+      // one probability per MFMA slot, packed in pairs a slot later (each exp result
+      // is used two instructions later or more), so every MFMA has a short block of
+      // vector work behind it rather than four exponentials behind every fourth one
+      // (long 1041 -> 1023 us, wide 367 -> 359, serving 251 -> 247)
+      float pe[16];
+      auto pack = [&](int k) __attribute__((always_inline)) {
+        pc[k] = pack2_bf16(pe[2 * k], pe[2 * k + 1]);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pc[k]), ones, sum, false);
+        pin(pc[k]);
         pin(sum);
       };
       constexpr int kAhead = 4;
@@ -852,11 +848,24 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         mfma(kOrder[r]);
         if (r + kAhead < 16) read(kOrder[r + kAhead]);
         __builtin_amdgcn_sched_barrier(0);
-        if ((r & 3) == 1) exp4(r >> 2);
+        if constexpr (kMma8) {
+          // (four every fourth slot here: this mode has two score MFMAs per half-step,
+          // and one exponential per slot measured 2% slower)
+          if ((r & 3) == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pe[r - 1 + e] = __builtin_amdgcn_exp2f(c[r - 1 + e] * c2 - mc);
+            pack((r - 1) >> 1);
+            pack(((r - 1) >> 1) + 1);
+          }
+        } else {
+          pe[r] = __builtin_amdgcn_exp2f(c[r] * c2 - mc);
+          if (r >= 2 && (r & 1) == 0) pack((r - 2) >> 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (r == kIssueAt) hook();
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (!kMma8) pack(7);
       l = l * al + sum;
       m_out = mr;
       if (__ballot(al != 1.0f)) {
