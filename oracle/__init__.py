@@ -23,7 +23,7 @@ from .tree import (ERR_BAD_PARENT, ERR_TOO_MANY_NODES, ERR_TOKEN, ERR_BLOCK, ERR
 from .attention import tree_attention
 from .acceptance import accept, accept_sequence, residual_token
 from .commit import commit_kv
-from .probs import softmax_rows
+from .probs import softmax_rows, softmax_rows_kept
 from .fp8 import e4m3_table, dequantize, tree_attention_fp8
 from .draft_tree import ERR_DRAFT, build_tree, build_trees
 from .philox import philox4x64, uniform24, node_uniforms
@@ -33,7 +33,7 @@ __all__ = [
     "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES", "ERR_TOKEN", "ERR_BLOCK", "ERR_ZERO_MASS",
     "ERR_PATH", "ERR_UNIFORM", "ancestors_or_self", "depths", "anc_bitsets", "build_index",
     "tree_attention", "accept", "accept_sequence", "residual_token", "commit_kv",
-    "softmax_rows", "e4m3_table", "dequantize", "tree_attention_fp8", "ERR_DRAFT", "build_tree",
+    "softmax_rows", "softmax_rows_kept", "e4m3_table", "dequantize", "tree_attention_fp8", "ERR_DRAFT", "build_tree",
     "build_trees", "philox4x64", "uniform24", "node_uniforms", "e4m3_round", "scale_shift",
     "quantize_rows", "dequantize_rows", "tree_attention_fp8mma",
 ]
