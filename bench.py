@@ -289,9 +289,25 @@ def measure_softmax(tv, case, reps: int) -> dict:
     us = float(np.median(times)) * 1e3
     bytes_ = 4 * case.vocab * (ctx + len(row_of))
     gbs = bytes_ / (us * 1e-6) / 1e9
+    # the draft's rows over a kept set of 64 tokens per context (tree_softmax_rows_kept):
+    # algorithmic bytes = every output row written + its 64 ids and logits read
+    keep_max = 64
+    keep = torch.from_numpy(np.stack([rng.choice(case.vocab, keep_max, replace=False)
+                                      for _ in range(ctx)]).astype(np.int32)).cuda()
+    run_k = lambda: tv.tree_softmax_rows_kept(lg, keep, ro, probs=probs, err=err)
+    run_k()
+    torch.cuda.synchronize()
+    us_k = graph_time_us(torch, run_k, n)
+    if int(err.item()) != 0:
+        raise SystemExit(f"kept rows: device error word {int(err.item())}")
+    bytes_k = len(row_of) * (4 * case.vocab + 8 * keep_max)
+    gbs_k = bytes_k / (us_k * 1e-6) / 1e9
+    kept = dict(us_per_call=round(us_k, 3), keep_max=keep_max, rows=len(row_of), alg_bytes=bytes_k,
+                achieved=round(gbs_k, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs_k / HBM_PEAK_GBS, 4), bound="hbm")
     return dict(us_per_call=round(us, 3), context_rows=ctx, rows=len(row_of), vocab=case.vocab,
                 alg_bytes=bytes_, achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm")
+                frac=round(gbs / HBM_PEAK_GBS, 4), bound="hbm", kept_rows=kept)
 
 
 def _graph_us(torch, run, reps: int) -> float:

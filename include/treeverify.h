@@ -22,6 +22,9 @@
  *   tree_draft_build      draft top-K rows -> parent array of the candidate tree
  * and a fourth that follows them:
  *   tree_commit_kv        the accepted path's K/V become prefix positions
+ * and the probability rows before acceptance (the draft's restricted to its kept
+ * set by the second):
+ *   tree_softmax_rows, tree_softmax_rows_kept
  * and a counter-based generator of the acceptance uniforms:
  *   tree_uniforms         per-node uniforms from (seed, request, tree level, node, step)
  * The three calls of the step also come as one call and as a HIP graph:
@@ -452,6 +455,38 @@ size_t tree_softmax_rows_workspace_size(int32_t ctx_rows, int32_t vocab);
 int tree_softmax_rows(const float* logits, int32_t ctx_rows, int32_t vocab, const int32_t* row_of,
                       int32_t rows, float inv_temperature, float* probs, void* workspace,
                       size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * tree_softmax_rows_kept — probability rows restricted to a kept set of tokens.
+ *
+ * Pruning the draft keeps a set R of candidates per context, so the drafted tokens
+ * come from q~(x) = q(x) * 1[x in R] / Z, Z the mass of R under q ([P525] §2.2.1);
+ * acceptance must divide by q~, not q.  [P525] §2.2.2 writes it as an edit of the
+ * logits before the softmax (log(1/Z) added on R, minus infinity elsewhere); the
+ * constant cancels, so a kept row is the softmax over R alone:
+ *   probs[i][k] = exp(t*logits[r][k] - M_R) / sum_{k' in R} exp(t*logits[r][k'] - M_R)
+ *   for k in R = the ids in keep[r], 0 elsewhere; r = row_of[i] (or i), M_R the
+ *   maximum of t*logits[r] over R.
+ * Meant for the draft's rows (p_draft of tree_accept); the target's rows stay the
+ * plain softmax of tree_softmax_rows.  fp32, relative error below 5e-6.
+ *
+ *   logits      [ctx_rows, vocab] float
+ *   keep        [ctx_rows, keep_max] int32: context row r's kept token ids; -1 is
+ *               padding and a repeated id counts once; keep_max in [1, 256]
+ *               (else TV_EUNSUPPORTED)
+ *   row_of      [rows] int32 or NULL (then rows == ctx_rows)
+ *   inv_temperature  t > 0
+ *   probs       out [rows, vocab] float.  The row is zero and a bit set when its
+ *               row_of entry is outside [0, ctx_rows) (TV_ERR_ROW), an id is
+ *               outside [-1, vocab) (TV_ERR_TOKEN) or the set is empty
+ *               (TV_ERR_ZERO_MASS)
+ * One kernel, one workgroup per output row; writes the whole row (HBM-bound on
+ * vocab * 4 bytes a row); no workspace.
+ */
+int tree_softmax_rows_kept(const float* logits, int32_t ctx_rows, int32_t vocab,
+                           const int32_t* keep, int32_t keep_max, const int32_t* row_of,
+                           int32_t rows, float inv_temperature, float* probs, int32_t* err,
+                           void* stream);
 
 /*
  * tree_verify_step — the step's three calls in one: tree_build_index, then

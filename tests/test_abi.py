@@ -247,6 +247,23 @@ def test_softmax_rows_host_checks(lib):
     assert tv.TV_ERR_ROW == oracle.probs.ERR_ROW
 
 
+def test_softmax_rows_kept_host_checks(lib):
+    one = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    call = lambda **kw: lib.tree_softmax_rows_kept(*{**dict(lg=one, c=4, v=1000, keep=one, km=8,
+                                                            row_of=None, r=4, t=1.0, p=one,
+                                                            err=one, s=None), **kw}.values())
+    assert call(km=0) == tv.TV_EUNSUPPORTED
+    assert call(km=257) == tv.TV_EUNSUPPORTED
+    assert b"keep_max" in lib.tree_last_error()
+    assert call(t=-1.0) == tv.TV_EINVAL
+    assert call(r=5) == tv.TV_EINVAL                 # rows != ctx_rows without row_of
+    assert call(v=-1) == tv.TV_EINVAL
+    assert call(err=None) == tv.TV_EINVAL
+    assert call(keep=None) == tv.TV_EINVAL
+    assert call(r=0, c=0) == tv.TV_OK                # nothing to do
+    assert (tv.TV_ERR_TOKEN, tv.TV_ERR_ZERO_MASS) == (oracle.ERR_TOKEN, oracle.ERR_ZERO_MASS)
+
+
 def test_uniforms_host_checks(lib):
     one = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
     assert lib.tree_uniforms(1, 0, 0, one, one, one, -1, 4, one, one, None) == tv.TV_EINVAL

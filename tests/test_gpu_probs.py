@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests._helpers import gpu_accept, oracle_accept
+from tests._helpers import assert_accept_equal, gpu_accept, oracle_accept
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +85,79 @@ def test_softmax_rows_feed_acceptance(gpu_lib):
     want = oracle_accept(case, 8)
     for k in ("accept_len", "path", "resample_node", "resample_token"):
         np.testing.assert_array_equal(np.asarray(got[k]), np.asarray(want[k]), err_msg=k)
+
+
+# ---- kept-set rows (the pruned draft distribution) --------------------------------
+
+def kept_sets(rng, ctx_rows, vocab, keep_max, pad=True):
+    """Per context row: a random number of distinct ids, some repeated, padded with -1."""
+    keep = np.full((ctx_rows, keep_max), -1, np.int32)
+    for r in range(ctx_rows):
+        k = int(rng.integers(1, keep_max + 1)) if pad else keep_max
+        ids = rng.choice(vocab, size=min(k, vocab), replace=False)
+        if k > 2 and pad:
+            ids[-1] = ids[0]            # a repeat counts once
+        keep[r, :len(ids)] = rng.permutation(ids)
+    return keep
+
+
+@pytest.mark.parametrize("ctx_rows,vocab,keep_max,t", [(7, 1000, 16, 1.0), (5, 3001, 64, 0.8),
+                                                       (3, 152064, 256, 1.0), (4, 32000, 1, 1.3),
+                                                       (2, 7, 8, 1.0)])
+def test_softmax_rows_kept_parity(gpu_lib, ctx_rows, vocab, keep_max, t):
+    rng = np.random.default_rng(vocab + keep_max)
+    lg = logits_rows(ctx_rows, vocab, seed=ctx_rows + vocab)
+    keep = kept_sets(rng, ctx_rows, vocab, keep_max)
+    row_of = rng.integers(0, ctx_rows, 2 * ctx_rows + 1).astype(np.int32)
+    got, err = gpu_lib.tree_softmax_rows_kept(torch.from_numpy(lg).cuda(), torch.from_numpy(keep).cuda(),
+                                              torch.from_numpy(row_of).cuda(), inv_temperature=t)
+    torch.cuda.synchronize()
+    want, werr = oracle.softmax_rows_kept(lg, keep, row_of=row_of, inv_temperature=t)
+    assert int(err.item()) == werr == 0
+    check(got.cpu().numpy(), want)
+    own, err2 = gpu_lib.tree_softmax_rows_kept(torch.from_numpy(lg).cuda(), torch.from_numpy(keep).cuda(),
+                                               inv_temperature=t)
+    torch.cuda.synchronize()
+    assert int(err2.item()) == 0
+    check(own.cpu().numpy(), oracle.softmax_rows_kept(lg, keep, inv_temperature=t)[0])
+
+
+def test_softmax_rows_kept_errors_leave_zero_rows(gpu_lib):
+    lg = logits_rows(3, 1001, seed=9)
+    keep = np.array([[5, 5, 900, -1], [-1, -1, -1, -1], [3, 1001, -1, -1]], np.int32)
+    row_of = np.array([0, 1, 2, 3, -1, 0], np.int32)
+    probs = torch.full((6, 1001), 7.0, device="cuda")        # every row must be overwritten
+    got, err = gpu_lib.tree_softmax_rows_kept(torch.from_numpy(lg).cuda(), torch.from_numpy(keep).cuda(),
+                                              torch.from_numpy(row_of).cuda(), probs=probs)
+    torch.cuda.synchronize()
+    want, werr = oracle.softmax_rows_kept(lg, keep, row_of=row_of)
+    assert werr == oracle.ERR_ZERO_MASS | oracle.ERR_TOKEN | oracle.probs.ERR_ROW
+    assert int(err.item()) == werr
+    check(got.cpu().numpy(), want)
+    assert not got[1:5].any()
+
+
+def test_kept_draft_rows_feed_acceptance(gpu_lib):
+    """Draft rows restricted to their kept sets are the p_draft of tree_accept: the
+    acceptance outputs match the oracle's on the same rows, bit for bit."""
+    rng = np.random.default_rng(11)
+    parents = W.tree_kary_levels(4, 3)          # 84 nodes, 21 contexts
+    row_of, ctx = context_rows(parents)
+    vocab = 5000
+    dl = logits_rows(ctx, vocab, seed=12)
+    tl = logits_rows(ctx, vocab, seed=13)
+    keep = kept_sets(rng, ctx, vocab, 32, pad=False)
+    n = len(parents)
+    token = np.array([keep[row_of[i], rng.integers(0, 32)] for i in range(n)], np.int32)
+    pd, e1 = gpu_lib.tree_softmax_rows_kept(torch.from_numpy(dl).cuda(), torch.from_numpy(keep).cuda(),
+                                            torch.from_numpy(row_of).cuda())
+    pt, e2 = gpu_lib.tree_softmax_rows(torch.from_numpy(tl).cuda(), torch.from_numpy(row_of).cuda())
+    torch.cuda.synchronize()
+    assert int(e1.item()) == int(e2.item()) == 0
+    case = W.make_case("kept", [parents], [100], 1, 1, 64, W.DT_F32, vocab, 14, with_probs=True)
+    case.p_target = pt.cpu().numpy()
+    case.p_draft = pd.cpu().numpy()
+    case.token = token
+    dev = W.case_to_device(case, probs=True)
+    got = gpu_accept(gpu_lib, case, dev, max_path=8)
+    assert_accept_equal(got, oracle_accept(case, max_path=8))

@@ -50,6 +50,7 @@ EXPORTS = (
     "tree_commit_kv",
     "tree_softmax_rows_workspace_size",
     "tree_softmax_rows",
+    "tree_softmax_rows_kept",
     "tree_uniforms",
     "tree_quantize_rows_e4m3",
     "tree_verify_step_args_size",
@@ -122,6 +123,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_softmax_rows_workspace_size.restype = Z
     lib.tree_softmax_rows.argtypes = [P, I, I, P, I, F, P, P, Z, P, P]
     lib.tree_softmax_rows.restype = ctypes.c_int
+    lib.tree_softmax_rows_kept.argtypes = [P, I, I, P, I, P, I, F, P, P, P]
+    lib.tree_softmax_rows_kept.restype = ctypes.c_int
     U64 = ctypes.c_uint64
     lib.tree_uniforms.argtypes = [U64, U64, U64, P, P, P, I, I, P, P, P]
     lib.tree_uniforms.restype = ctypes.c_int
@@ -548,6 +551,33 @@ def tree_softmax_rows(logits, row_of=None, *, inv_temperature: float = 1.0, prob
            lib.tree_softmax_rows(_ptr(logits), ctx_rows, vocab, _ptr(row_of), rows,
                                  float(inv_temperature), _ptr(probs), _ptr(workspace),
                                  workspace.numel(), _ptr(err), _stream(stream)))
+    return probs, err
+
+
+def tree_softmax_rows_kept(logits, keep, row_of=None, *, inv_temperature: float = 1.0,
+                           probs=None, err=None, stream=None):
+    """Probability rows over each context row's kept set (keep [ctx_rows, keep_max]
+    int32 token ids, -1 = padding), zero elsewhere: the pruned draft distribution.
+    Returns (probs [rows, vocab] float32, err)."""
+    lib = load()
+    _need(logits, "logits", torch.float32, 2)
+    _need(keep, "keep", torch.int32, 2)
+    ctx_rows, vocab = logits.shape
+    if keep.shape[0] != ctx_rows:
+        raise ValueError("keep must have one row per logits row")
+    if row_of is not None:
+        _need(row_of, "row_of", torch.int32, 1)
+    rows = ctx_rows if row_of is None else row_of.numel()
+    if probs is None:
+        probs = torch.empty((rows, vocab), dtype=torch.float32, device=logits.device)
+    _need(probs, "probs", torch.float32, 2)
+    if tuple(probs.shape) != (rows, vocab):
+        raise ValueError("probs must be [rows, vocab]")
+    err = _err_word(err, logits.device)
+    _check("tree_softmax_rows_kept",
+           lib.tree_softmax_rows_kept(_ptr(logits), ctx_rows, vocab, _ptr(keep), keep.shape[1],
+                                      _ptr(row_of), rows, float(inv_temperature), _ptr(probs),
+                                      _ptr(err), _stream(stream)))
     return probs, err
 
 

@@ -13,6 +13,13 @@
 // of a row and writes one chunk of probabilities for 8 consecutive output rows,
 // loading a context chunk once for a run of siblings.  Logits are read twice
 // (once per pass), probabilities written once.
+//
+// tree_softmax_rows_kept: the same rows restricted to a kept set of tokens per
+// context row, zero elsewhere -- the distribution a pruned draft actually samples
+// from, q~ = q * 1[x in R] / Z (page "端侧大模型推测解码草稿模型动态剪枝策略…" (ufo.work/
+// 2026/525), §2.2.1; §2.2.2's edit of the logits, log(1/Z) on the kept tokens and
+// minus infinity elsewhere, gives the same softmax because the constant cancels).
+// One workgroup per output row (k_row_keep).
 #include <algorithm>
 
 #include "tv_common.h"
@@ -164,6 +171,67 @@ __global__ void __launch_bounds__(kRowThreads) k_row_write(RowArgs a) {
   }
 }
 
+constexpr int kKeepMax = kRowThreads;  // kept ids per context row: one per thread
+
+struct KeptArgs {
+  const float* logits;
+  const int32_t* keep;    // [ctx_rows, keep_max], -1 = padding
+  const int32_t* row_of;
+  float* probs;
+  int32_t* err;
+  int ctx_rows, rows, vocab, keep_max;
+  float t;
+};
+
+// Output row i: the kept ids of its context row r go to LDS; an id that repeats an
+// earlier entry, or is padding, drops out; the kept logits are gathered and reduced
+// to (max, sum of exp); the row is zero-filled by streaming stores and, once those
+// have completed (so no zero lands after a probability), the kept probabilities are
+// written.  A bad context row index, an id outside [-1, vocab) or an empty set
+// leaves the row zero and sets its error bit.
+template <bool kVec>
+__global__ void __launch_bounds__(kRowThreads) k_row_keep(KeptArgs a) {
+  __shared__ int s_ids[kKeepMax];
+  __shared__ float2 s_red[kRowThreads / 64];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const long i = blockIdx.x;
+  const int r = a.row_of != nullptr ? a.row_of[i] : static_cast<int>(i);
+  const bool row_ok = r >= 0 && r < a.ctx_rows;
+  if (tid == 0) s_bad = row_ok ? 0 : TV_ERR_ROW;
+  __syncthreads();
+  int id = -1;
+  if (row_ok && tid < a.keep_max) {
+    id = a.keep[static_cast<long>(r) * a.keep_max + tid];
+    if (id < -1 || id >= a.vocab) atomicOr(&s_bad, TV_ERR_TOKEN);
+    s_ids[tid] = id;
+  }
+  __syncthreads();
+  const int bad_in = s_bad;
+  if (bad_in != 0) id = -1;
+  if (id >= 0)
+    for (int j = 0; j < tid; ++j)
+      if (s_ids[j] == id) {
+        id = -1;
+        break;
+      }
+  const float x = id >= 0 ? a.t * a.logits[static_cast<long>(r) * a.vocab + id] : -INFINITY;
+  float m = x, sum = id >= 0 ? 1.0f : 0.0f;
+  block_stat(m, sum, s_red);
+  float* out = a.probs + i * a.vocab;
+  if (kVec) {
+    for (int k = 4 * tid; k < a.vocab; k += 4 * kRowThreads)
+      __builtin_nontemporal_store(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, reinterpret_cast<f32x4_t*>(out + k));
+  } else {
+    for (int k = tid; k < a.vocab; k += kRowThreads) __builtin_nontemporal_store(0.0f, out + k);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's zeros have landed
+  __syncthreads();
+  const int bad = bad_in | (bad_in == 0 && m == -INFINITY ? TV_ERR_ZERO_MASS : 0);
+  if (bad == 0 && id >= 0) out[id] = expf(x - m) / sum;
+  if (tid == 0 && bad != 0) atomicOr(a.err, bad);
+}
+
 }  // namespace
 
 }  // namespace tv
@@ -226,4 +294,45 @@ extern "C" int tree_softmax_rows(const float* logits, int32_t ctx_rows, int32_t 
   else
     hipLaunchKernelGGL(tv::k_row_write<false>, dim3(chunks, groups), dim3(tv::kRowThreads), 0, s, a);
   return tv::check_launch("tree_softmax_rows/write");
+}
+
+extern "C" int tree_softmax_rows_kept(const float* logits, int32_t ctx_rows, int32_t vocab,
+                                      const int32_t* keep, int32_t keep_max, const int32_t* row_of,
+                                      int32_t rows, float inv_temperature, float* probs,
+                                      int32_t* err, void* stream) {
+  tv::clear_error();
+  if (ctx_rows < 0 || rows < 0 || vocab < 0)
+    return tv::fail(TV_EINVAL, "tree_softmax_rows_kept: negative size");
+  if (keep_max < 1 || keep_max > tv::kKeepMax)
+    return tv::fail(TV_EUNSUPPORTED, "tree_softmax_rows_kept: keep_max must be in [1, 256]");
+  if (!(inv_temperature > 0.0f) || inv_temperature == INFINITY)
+    return tv::fail(TV_EINVAL,
+                    "tree_softmax_rows_kept: inverse temperature must be positive and finite");
+  if (row_of == nullptr && rows != ctx_rows)
+    return tv::fail(TV_EINVAL, "tree_softmax_rows_kept: without row_of, rows must equal ctx_rows");
+  if (err == nullptr) return tv::fail(TV_EINVAL, "tree_softmax_rows_kept: null err");
+  if (rows == 0 || vocab == 0) return TV_OK;
+  if (ctx_rows == 0) return tv::fail(TV_EINVAL, "tree_softmax_rows_kept: rows without context rows");
+  if (logits == nullptr || probs == nullptr || keep == nullptr)
+    return tv::fail(TV_EINVAL, "tree_softmax_rows_kept: null logits, keep or probs");
+  if (static_cast<long>(ctx_rows) * vocab > (1L << 40) || static_cast<long>(rows) * vocab > (1L << 40))
+    return tv::fail(TV_EUNSUPPORTED, "tree_softmax_rows_kept: rows too large");
+  tv::KeptArgs a{};
+  a.logits = logits;
+  a.keep = keep;
+  a.row_of = row_of;
+  a.probs = probs;
+  a.err = err;
+  a.ctx_rows = ctx_rows;
+  a.rows = rows;
+  a.vocab = vocab;
+  a.keep_max = keep_max;
+  a.t = inv_temperature;
+  auto s = static_cast<hipStream_t>(stream);
+  const bool vec = vocab % 4 == 0 && (reinterpret_cast<uintptr_t>(probs) % 16) == 0;
+  if (vec)
+    hipLaunchKernelGGL(tv::k_row_keep<true>, dim3(rows), dim3(tv::kRowThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(tv::k_row_keep<false>, dim3(rows), dim3(tv::kRowThreads), 0, s, a);
+  return tv::check_launch("tree_softmax_rows_kept");
 }
