@@ -16,12 +16,14 @@
 // One wavefront per sequence.  The truncation and weights of every row are
 // computed before the draws (all rows are inputs); the weights, the uniforms and
 // the candidates (in creation order) live in LDS, so a draw waits on no global
-// memory.  A draw
-// sums the weights in 64 contiguous chunks (one per lane), scans the chunk sums
-// across the wavefront (DPP), and the lane whose chunk holds u * total walks it.  The
-// truncation and the normaliser of the weights are summed by one lane in slot
-// order; powers are one per lane.  Everything that decides a draw is fp64 with
-// no contraction.
+// memory.  Lane c keeps the sum of the weights of candidates 128c .. 128c + 127 in
+// a register (new candidates join it as they are created; the chunk a draw takes
+// from is summed afresh).  A draw scans the chunk sums across the wavefront (DPP),
+// the first chunk whose running sum passes u * total is read by the whole
+// wavefront, two candidates a lane, in one LDS round trip, and a second scan finds
+// the candidate.  The truncation and the normaliser of the weights are summed by
+// one lane in slot order; powers are one per lane.  Everything that decides a
+// draw is fp64 with no contraction.
 #include "tv_common.h"
 
 #pragma clang fp contract(off)
@@ -33,6 +35,10 @@ namespace {
 constexpr int kMaxDraftNodes = 256;
 constexpr int kMaxDraftK = 16;
 constexpr int kMaxCand = kMaxDraftK * (kMaxDraftNodes + 1);
+constexpr int kChunk = 128;                                // candidates per lane's chunk
+constexpr int kChunks = (kMaxCand + kChunk - 1) / kChunk;  // 33
+constexpr int kCandCap = kChunks * kChunk;                 // whole chunks are read
+static_assert(kChunks <= 64, "one chunk per lane");
 
 struct DraftArgs {
   const float* probs;  // [batch, rows, k]
@@ -84,32 +90,43 @@ __device__ __forceinline__ double wave_incl_scan(double x) {
   return x;
 }
 
-// candidate info: context node + 1 (9 bits), slot (4 bits); depth comes from the node
-__device__ __forceinline__ uint16_t pack_info(int ctx, int slot) {
-  return static_cast<uint16_t>((ctx + 1) | (slot << 9));
+// a double of lane `src` (uniform) in every lane
+__device__ __forceinline__ double readlane_f64(double x, int src) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), src),
+                          __builtin_amdgcn_readlane(__double2loint(x), src));
+}
+
+// candidate info: context node + 1 (9 bits), slot (4 bits), depth of the node it
+// would become (9 bits)
+__device__ __forceinline__ uint32_t pack_info(int ctx, int slot, int depth) {
+  return static_cast<uint32_t>((ctx + 1) | (slot << 9) | (depth << 13));
 }
 
 // LDS layout (bytes): candidates' path weights and info, then per (row, slot)
 // importance weights and renormalised probabilities, then per row / node scalars
 constexpr int kRowSlots = (kMaxDraftNodes + 1) * kMaxDraftK;
 constexpr int kOffW = 0;
-constexpr int kOffWRow = kOffW + kMaxCand * 8;  // reads up to 3 entries past s_w land here
+constexpr int kOffWRow = kOffW + kCandCap * 8;
 constexpr int kOffQ = kOffWRow + kRowSlots * 8;
-constexpr int kOffInfo = kOffQ + kRowSlots * 4;
-constexpr int kOffU = kOffInfo + kMaxCand * 2;
-constexpr int kOffDepth = kOffU + kMaxDraftNodes * 4;
-constexpr int kOffM = kOffDepth + kMaxDraftNodes * 2;
-constexpr int kDraftLds = kOffM + kMaxDraftNodes + 8;
+constexpr int kOffInfo = kOffQ + kRowSlots * 4;  // whole chunks are read
+constexpr int kOffU = kOffInfo + kCandCap * 4;
+constexpr int kOffM = kOffU + kMaxDraftNodes * 4;
+// the built nodes' outputs, written out once after the draws (so a draw never
+// waits for a global store to complete)
+constexpr int kOffPOut = (kOffM + kMaxDraftNodes + 8 + 1) & ~1;
+constexpr int kOffSOut = kOffPOut + kMaxDraftNodes * 2;
+constexpr int kDraftLds = kOffSOut + kMaxDraftNodes;
 
 __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   double* s_w = reinterpret_cast<double*>(smem + kOffW);        // path weight; 0 once taken
   double* s_wrow = reinterpret_cast<double*>(smem + kOffWRow);  // importance weight (row, slot)
   float* s_q = reinterpret_cast<float*>(smem + kOffQ);          // p / kept mass (row, slot)
-  uint16_t* s_info = reinterpret_cast<uint16_t*>(smem + kOffInfo);
+  uint32_t* s_info = reinterpret_cast<uint32_t*>(smem + kOffInfo);
   float* s_u = reinterpret_cast<float*>(smem + kOffU);
-  int16_t* s_depth = reinterpret_cast<int16_t*>(smem + kOffDepth);
   uint8_t* s_m = reinterpret_cast<uint8_t*>(smem + kOffM);      // kept slots of each row
+  int16_t* s_po = reinterpret_cast<int16_t*>(smem + kOffPOut);
+  uint8_t* s_so = reinterpret_cast<uint8_t*>(smem + kOffSOut);
   const int b = blockIdx.x, lane = threadIdx.x;
   const float* P = a.probs + static_cast<long>(b) * a.rows * a.k;
   const float* U = a.u + static_cast<long>(b) * a.n_max;
@@ -117,11 +134,6 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
   int32_t* slot = a.slot + static_cast<long>(b) * a.n_max;
   float* qd = a.q_draft + static_cast<long>(b) * a.n_max;
 
-  for (int i = lane; i < a.n_max; i += 64) {  // padding past the count
-    parent[i] = -2;
-    slot[i] = -2;
-    qd[i] = 0.0f;
-  }
   bool bad_p = false, bad_u = false;
   for (int i = lane; i < a.rows * a.k; i += 64) {
     const float p = P[i];
@@ -134,6 +146,11 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
   }
   const int bad = (__ballot(bad_p) ? TV_ERR_DRAFT : 0) | (__ballot(bad_u) ? TV_ERR_UNIFORM : 0);
   if (bad) {
+    for (int i = lane; i < a.n_max; i += 64) {  // no nodes: all padding
+      parent[i] = -2;
+      slot[i] = -2;
+      qd[i] = 0.0f;
+    }
     if (lane == 0) {
       atomicOr(a.err, bad);
       a.count[b] = 0;
@@ -179,77 +196,106 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
   }
   __syncthreads();
 
+  for (int j = lane; j < kCandCap; j += 64) s_w[j] = 0.0;  // whole chunks are read
+  __syncthreads();
+
   int n_cand = 0;
-  // candidates of context row `row` (node ctx, -1 = prefix) appended in slot order
-  auto expand = [&](int row, int ctx, double ctx_pw) __attribute__((always_inline)) {
-    const int m = s_m[row];
+  double cs = 0.0;  // lane c: sum of the weights of candidates kChunk c .. kChunk (c + 1) - 1
+  // candidates of a context row appended in slot order: m kept slots, this lane's
+  // weight w (0 past m), info for slot `lane`; each new weight joins its chunk's sum
+  // in that order
+  auto expand = [&](int m, double w, uint32_t info) __attribute__((always_inline)) {
     if (lane < m) {
-      s_w[n_cand + lane] = ctx_pw * s_wrow[row * a.k + lane];
-      s_info[n_cand + lane] = pack_info(ctx, lane);
+      s_w[n_cand + lane] = w;
+      s_info[n_cand + lane] = info;
+    }
+    // the new weights' sum per chunk (they span at most two: m <= 16 < kChunk), one
+    // running sum per chunk over its lanes rather than one lane read per candidate;
+    // each is a sum of that chunk's new weights alone, so it is 0 exactly when they
+    // all are
+    const int c_lo = n_cand / kChunk, split = min(m, (c_lo + 1) * kChunk - n_cand);
+    if (split > 0) {
+      const double lo = readlane_f64(wave_incl_scan(lane < split ? w : 0.0), split - 1);
+      if (lane == c_lo) cs += lo;
+    }
+    if (split < m) {
+      const double hi = readlane_f64(wave_incl_scan(lane >= split ? w : 0.0), m - 1);
+      if (lane == c_lo + 1) cs += hi;
     }
     n_cand += m;
     __syncthreads();
   };
 
-  expand(0, -1, 1.0);
+  {
+    const int m0 = s_m[0];
+    expand(m0, lane < m0 ? s_wrow[lane] : 0.0, pack_info(-1, lane, 1));
+  }
   int n = 0;
   for (; n < a.n_max; ++n) {
-    // chunk sums, then a scan of them across the wavefront
-    const int chunk = (n_cand + 63) / 64;
-    const int c0 = min(n_cand, lane * chunk), c1 = min(n_cand, c0 + chunk);
-    // weights read 4 at a time (the LDS latency once per 4), added in candidate order;
-    // entries past the chunk are read (inside the LDS block: s_wrow follows s_w) but
-    // count as +0.0, which leaves a sum of non-negative weights unchanged
-    double ls = 0.0;
-    for (int j = c0; j < c1; j += 4) {
-      double v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = s_w[j + e];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ls += j + e < c1 ? v[e] : 0.0;
-    }
-    const double incl = wave_incl_scan(ls);
+    // the row a node drawn now would expand (row n + 1), read ahead of the draw
+    const bool has_row = n + 1 < a.rows;
+    const int m_next = has_row ? s_m[n + 1] : 0;
+    const double w_next = lane < m_next ? s_wrow[(n + 1) * a.k + lane] : 0.0;
+    const double incl = wave_incl_scan(cs);
     const double excl = dpp_shift(incl, 0x138, 0xf);  // wave_shr:1; lane 0 gets 0
-    const double total = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(incl), 63),
-                                          __builtin_amdgcn_readlane(__double2loint(incl), 63));
+    const double total = readlane_f64(incl, 63);
     if (!(total > 0.0)) break;
     const double t = static_cast<double>(s_u[n]) * total;
+    // the chunk: the first whose running sum passes t (lane 63's always does, as
+    // u < 1); it holds weight, since adding a zero chunk leaves every partial sum
     const unsigned long long over = __ballot(incl > t);
-    const int owner = over ? __ffsll(static_cast<long long>(over)) - 1 : 63;
-    int pick = -1;
-    if (lane == owner) {
-      double run = excl;
-      int last = -1;
-      for (int j = c0; j < c1 && pick < 0; j += 4) {  // 4 weights per LDS round trip
-        double v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = s_w[j + e];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (pick >= 0 || j + e >= c1) continue;
-          if (v[e] > 0.0) last = j + e;
-          run += v[e];
-          if (run > t) pick = j + e;
-        }
-      }
-      if (pick < 0) pick = last;  // rounding left the chunk's walk short: its last live entry
+    const int owner = min(over ? __ffsll(static_cast<long long>(over)) - 1 : kChunks - 1, kChunks - 1);
+    const double base = readlane_f64(excl, owner);
+    // the chunk's candidates, two a lane (weights and info), and their running sums
+    const double2 v = *reinterpret_cast<const double2*>(s_w + owner * kChunk + 2 * lane);
+    const uint2 vi = *reinterpret_cast<const uint2*>(s_info + owner * kChunk + 2 * lane);
+    const double ps = v.x + v.y;
+    const double pincl = wave_incl_scan(ps);
+    const double pexcl = dpp_shift(pincl, 0x138, 0xf);
+    const unsigned long long hit = __ballot(base + pincl > t);
+    int jl, sel;
+    if (hit) {
+      jl = __ffsll(static_cast<long long>(hit)) - 1;
+    } else {
+      // rounding left the chunk's running sum short of t: its last candidate with weight
+      const unsigned long long live = __ballot(v.x > 0.0 || v.y > 0.0);
+      if (!live) break;  // unreachable: the chunk's sum is positive
+      jl = 63 - __clzll(static_cast<long long>(live));
     }
-    pick = __shfl(pick, owner, 64);
-    if (pick < 0) break;  // unreachable while total > 0 and u < 1; keeps the LDS index valid
-    const int info = s_info[pick];
-    const double pw = s_w[pick];
-    const int ctx = (info & 511) - 1, sl = (info >> 9) & 15;
-    const int dep = ctx < 0 ? 1 : s_depth[ctx] + 1;
-    __syncthreads();
+    const double vx = readlane_f64(v.x, jl), vy = readlane_f64(v.y, jl);
+    if (hit) {
+      // its first candidate if it passes t on its own; a candidate without weight
+      // is never taken (the scan's rounding cannot make an empty pair pass)
+      const double pe = readlane_f64(pexcl, jl);
+      sel = (vx > 0.0 && (vy == 0.0 || base + pe + vx > t)) ? 0 : 1;
+    } else {
+      sel = vy > 0.0 ? 1 : 0;
+    }
+    const int pick = owner * kChunk + 2 * jl + sel;
+    // the chunk's sum without the taken candidate, summed afresh
+    // (read out in every lane: a read of lane 63 inside the owner's branch would let
+    // the compiler finish the scan there, where lane 63 is inactive)
+    const double rest = readlane_f64(wave_incl_scan(lane == jl ? (sel ? v.x : v.y) : ps), 63);
+    if (lane == owner) cs = rest;
+    const uint32_t info = __builtin_amdgcn_readlane(sel ? vi.y : vi.x, jl);
+    const double pw = sel ? vy : vx;
+    const int ctx = static_cast<int>(info & 511) - 1, sl = (info >> 9) & 15;
+    const int dep = static_cast<int>(info >> 13);
     if (lane == 0) {
-      parent[n] = ctx;
-      slot[n] = sl;
-      qd[n] = s_q[(ctx + 1) * a.k + sl];  // renormalised by the kept mass of its context row
+      s_po[n] = static_cast<int16_t>(ctx);
+      s_so[n] = static_cast<uint8_t>(sl);
       s_w[pick] = 0.0;
-      s_depth[n] = static_cast<int16_t>(dep);
     }
     __syncthreads();
-    if (dep < a.max_depth && n + 1 < a.rows) expand(n + 1, n, pw);
+    if (dep < a.max_depth && has_row) expand(m_next, pw * w_next, pack_info(n, lane, dep + 1));
+  }
+  __syncthreads();
+  for (int i = lane; i < a.n_max; i += 64) {  // the nodes, then padding past the count
+    const int c = i < n ? s_po[i] : -2, sl = i < n ? s_so[i] : -2;
+    parent[i] = c;
+    slot[i] = sl;
+    // q_draft: renormalised by the kept mass of the node's context row
+    qd[i] = i < n ? s_q[(c + 1) * a.k + sl] : 0.0f;
   }
   if (lane == 0) a.count[b] = n;
 }
