@@ -272,10 +272,14 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
       sel = vy > 0.0 ? 1 : 0;
     }
     const int pick = owner * kChunk + 2 * jl + sel;
-    // the chunk's sum without the taken candidate, summed afresh
-    // (read out in every lane: a read of lane 63 inside the owner's branch would let
-    // the compiler finish the scan there, where lane 63 is inactive)
-    const double rest = readlane_f64(wave_incl_scan(lane == jl ? (sel ? v.x : v.y) : ps), 63);
+    // the chunk's sum without the taken candidate: its fresh sum minus the taken
+    // weight.  Never negative (a sum of non-negative weights is at least each of
+    // them) and 0 exactly when the taken one was its last (adding zeros is exact);
+    // only remaining weights below the sum's rounding can be left out, until the
+    // chunk gains a candidate.  (Read out in every lane: a read of lane 63 inside the
+    // owner's branch would let the compiler finish the scan there, where lane 63 is
+    // inactive.)
+    const double rest = readlane_f64(pincl, 63) - (sel ? vy : vx);
     if (lane == owner) cs = rest;
     const uint32_t info = __builtin_amdgcn_readlane(sel ? vi.y : vi.x, jl);
     const double pw = sel ? vy : vx;
