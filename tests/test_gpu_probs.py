@@ -161,3 +161,40 @@ def test_kept_draft_rows_feed_acceptance(gpu_lib):
     dev = W.case_to_device(case, probs=True)
     got = gpu_accept(gpu_lib, case, dev, max_path=8)
     assert_accept_equal(got, oracle_accept(case, max_path=8))
+
+
+def test_kept_rows_agree_with_the_draft_tree(gpu_lib):
+    """The draft tree builder judges a drafted token by its top-K probability over its
+    context's kept mass (q_draft); the kept-set row of the same context's draft
+    logits, with the kept slots' tokens as the set, gives the same number at that
+    token (two routes to q~ of page [P525] §2.2.1)."""
+    from oracle.draft_tree import kept_count
+    rng = np.random.default_rng(21)
+    n_max, vocab, k, ratio = 48, 4096, 8, 0.1
+    ctx = n_max + 1
+    lg = (rng.standard_normal((ctx, vocab)) * 3.0).astype(np.float32)   # peaked: truncation bites
+    lg_t = torch.from_numpy(lg).cuda()
+    full = torch.softmax(lg_t.double(), dim=1)
+    p_top, tok_top = torch.topk(full, k, dim=1)                        # non-increasing slots
+    probs = p_top.float().contiguous()[None]
+    u = torch.from_numpy(W.grid_uniforms(rng, n_max).astype(np.float32)[None]).cuda()
+    parent, slot, qd, count, err = gpu_lib.tree_draft_build(probs, u, 5, 0.7, ratio)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    n = int(count[0].item())
+    assert n > 1
+    p_np, tok_np = probs[0].cpu().numpy(), tok_top.cpu().numpy()
+    keep = np.full((ctx, k), -1, np.int32)
+    for r in range(ctx):
+        m, _ = kept_count(p_np[r], ratio)
+        keep[r, :m] = tok_np[r, :m]
+    par, sl = parent[0, :n].cpu().numpy(), slot[0, :n].cpu().numpy()
+    row_of = (par + 1).astype(np.int32)                                 # context after the parent
+    pd, err2 = gpu_lib.tree_softmax_rows_kept(lg_t, torch.from_numpy(keep).cuda(),
+                                              torch.from_numpy(row_of).cuda())
+    torch.cuda.synchronize()
+    assert int(err2.item()) == 0
+    tokens = tok_np[row_of, sl]
+    got = pd.cpu().numpy()[np.arange(n), tokens].astype(np.float64)
+    want = qd[0, :n].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got, want, rtol=2e-5, atol=0)
