@@ -80,4 +80,6 @@ def assert_accept_equal(got: dict, want: dict):
     for k in ("accept_len", "path", "resample_node", "resample_token", "node_ok"):
         np.testing.assert_array_equal(np.asarray(got[k]).astype(np.int64),
                                       np.asarray(want[k]).astype(np.int64), err_msg=k)
-    assert int(got["err"][0]) == int(want["err"]), (int(got["err"][0]), want["err"])
+    got_err = int(np.asarray(got["err"]).reshape(-1)[0])
+    want_err = int(np.asarray(want["err"]).reshape(-1)[0])
+    assert got_err == want_err, (got_err, want_err)
