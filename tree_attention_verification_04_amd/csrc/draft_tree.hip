@@ -78,13 +78,19 @@ __device__ __forceinline__ double dpp_shift(double x, int ctrl, int row_mask) {
   return __hiloint2double(hi2, lo2);
 }
 
-// inclusive prefix sum over the 64 lanes: shifts 1, 2, 4, 8 inside each 16-lane
-// row, then the row totals broadcast into the rows after them
-__device__ __forceinline__ double wave_incl_scan(double x) {
+// inclusive prefix sum inside each 16-lane row (shifts 1, 2, 4, 8)
+__device__ __forceinline__ double row_incl_scan(double x) {
   x += dpp_shift(x, 0x111, 0xf);
   x += dpp_shift(x, 0x112, 0xf);
   x += dpp_shift(x, 0x114, 0xf);
   x += dpp_shift(x, 0x118, 0xf);
+  return x;
+}
+
+// inclusive prefix sum over the 64 lanes: the row scans, then the row totals
+// broadcast into the rows after them (lanes 0-15 end as the row scan left them)
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x = row_incl_scan(x);
   x += dpp_shift(x, 0x142, 0xa);
   x += dpp_shift(x, 0x143, 0xc);
   return x;
@@ -212,18 +218,21 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
     // the new weights' sum per chunk (they span at most two: m <= 16 < kChunk), one
     // running sum per chunk over its lanes rather than one lane read per candidate;
     // each is a sum of that chunk's new weights alone, so it is 0 exactly when they
-    // all are
+    // all are.  The new weights sit in lanes 0 .. m - 1 (m <= 16), one DPP row, so a
+    // row scan is the whole scan there.
     const int c_lo = n_cand / kChunk, split = min(m, (c_lo + 1) * kChunk - n_cand);
     if (split > 0) {
-      const double lo = readlane_f64(wave_incl_scan(lane < split ? w : 0.0), split - 1);
+      const double lo = readlane_f64(row_incl_scan(lane < split ? w : 0.0), split - 1);
       if (lane == c_lo) cs += lo;
     }
     if (split < m) {
-      const double hi = readlane_f64(wave_incl_scan(lane >= split ? w : 0.0), m - 1);
+      const double hi = readlane_f64(row_incl_scan(lane >= split ? w : 0.0), m - 1);
       if (lane == c_lo + 1) cs += hi;
     }
     n_cand += m;
-    __syncthreads();
+    // one wavefront: its LDS accesses complete in issue order, so a later read sees
+    // these writes; only the compiler must keep the order
+    __builtin_amdgcn_wave_barrier();
   };
 
   {
@@ -231,24 +240,28 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
     expand(m0, lane < m0 ? s_wrow[lane] : 0.0, pack_info(-1, lane, 1));
   }
   int n = 0;
+  int m_next = 1 < a.rows ? s_m[1] : 0;  // kept count of row n + 1
   for (; n < a.n_max; ++n) {
-    // the row a node drawn now would expand (row n + 1), read ahead of the draw
+    // the row a node drawn now would expand (row n + 1), read ahead of the draw (all
+    // of its first k slots, masked by the kept count when the candidates are made)
     const bool has_row = n + 1 < a.rows;
-    const int m_next = has_row ? s_m[n + 1] : 0;
-    const double w_next = lane < m_next ? s_wrow[(n + 1) * a.k + lane] : 0.0;
+    const double w_row = s_wrow[(has_row ? n + 1 : 0) * a.k + min(lane, a.k - 1)];
+    const float u_n = s_u[n];
     const double incl = wave_incl_scan(cs);
     const double excl = dpp_shift(incl, 0x138, 0xf);  // wave_shr:1; lane 0 gets 0
     const double total = readlane_f64(incl, 63);
-    if (!(total > 0.0)) break;
-    const double t = static_cast<double>(s_u[n]) * total;
+    const double t = static_cast<double>(u_n) * total;
     // the chunk: the first whose running sum passes t (lane 63's always does, as
     // u < 1); it holds weight, since adding a zero chunk leaves every partial sum
     const unsigned long long over = __ballot(incl > t);
+    if (!(total > 0.0)) break;  // (tested after the ballot: one block with the reads above)
     const int owner = min(over ? __ffsll(static_cast<long long>(over)) - 1 : kChunks - 1, kChunks - 1);
     const double base = readlane_f64(excl, owner);
     // the chunk's candidates, two a lane (weights and info), and their running sums
     const double2 v = *reinterpret_cast<const double2*>(s_w + owner * kChunk + 2 * lane);
     const uint2 vi = *reinterpret_cast<const uint2*>(s_info + owner * kChunk + 2 * lane);
+    // the next draw's kept count, read beside the chunk (no LDS wait of its own)
+    const int m_after = n + 2 < a.rows ? s_m[n + 2] : 0;
     const double ps = v.x + v.y;
     const double pincl = wave_incl_scan(ps);
     const double pexcl = dpp_shift(pincl, 0x138, 0xf);
@@ -290,8 +303,10 @@ __global__ void __launch_bounds__(64) k_draft_build(DraftArgs a) {
       s_so[n] = static_cast<uint8_t>(sl);
       s_w[pick] = 0.0;
     }
-    __syncthreads();
-    if (dep < a.max_depth && has_row) expand(m_next, pw * w_next, pack_info(n, lane, dep + 1));
+    __builtin_amdgcn_wave_barrier();  // (one wavefront: see expand)
+    if (dep < a.max_depth && has_row)
+      expand(m_next, lane < m_next ? pw * w_row : 0.0, pack_info(n, lane, dep + 1));
+    m_next = m_after;
   }
   __syncthreads();
   for (int i = lane; i < a.n_max; i += 64) {  // the nodes, then padding past the count
