@@ -30,6 +30,9 @@ CASES = {
     "uniform_weights": (4, 33, 6, 32, 4, 0.0, 0.2),
     "one_candidate": (2, 40, 1, 40, 40, 0.7, 0.1),
     "few_rows": (2, 10, 8, 64, 6, 0.7, 0.1),
+    # every limit at once: 256 draws, 16 slots a row, no truncation, no depth cap
+    # (up to 16 * 257 candidates, all 33 chunks of the candidate store in use)
+    "max_size": (2, 257, 16, 256, 256, 0.7, 0.0),
 }
 
 
