@@ -448,7 +448,11 @@ int tree_commit_kv(const void* k_tree, const void* v_tree, const int32_t* cu_nod
  *               [0, ctx_rows) is zero-filled and sets TV_ERR_ROW
  *   workspace   >= tree_softmax_rows_workspace_size(ctx_rows, vocab) bytes; no
  *               initial contents needed; calls sharing one must not overlap
- * Two kernels, HBM-bound; rows and vocab / 8192 at most 65535.
+ * HBM-bound.  With at least 256 output rows, a vocabulary that is a multiple of 4
+ * in [90112, 155136] and 16-byte aligned logits and probs, one kernel holds each
+ * context row on one compute unit and reads it once (the workspace is then not
+ * touched); otherwise two kernels read it twice.  rows and vocab / 8192 at most
+ * 65535.
  */
 size_t tree_softmax_rows_workspace_size(int32_t ctx_rows, int32_t vocab);
 

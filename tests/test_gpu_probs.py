@@ -69,6 +69,34 @@ def test_softmax_rows_bad_index_and_large_logits(gpu_lib):
     check(g[[0, 2, 4]], want[[0, 2, 4]])
 
 
+# The one-pass kernel (a context row held on one compute unit) runs for at least
+# 256 output rows with a vocabulary in [90112, 130560] (88 floats a thread in
+# registers, the rest in LDS) or [114688, 155136] (112 a thread): its edges (no LDS
+# part; the largest LDS part of each instance), both instances, groups of one and
+# of two output rows, shared contexts and bad context indices.
+@pytest.mark.parametrize("vocab,levels", [(90112, (4, 4)), (128256, (8, 3)), (130560, (4, 4)),
+                                          (131072, (4, 4)), (152064, (8, 3)), (155136, (4, 4))])
+def test_softmax_rows_one_pass(gpu_lib, vocab, levels):
+    parents = W.tree_kary_levels(*levels)   # 340 nodes / 85 contexts, 584 / 73
+    row_of, ctx = context_rows(parents)
+    row_of[5] = -1
+    row_of[-1] = ctx
+    lg = logits_rows(ctx, vocab, seed=vocab + ctx)
+    lg[1, 17] = np.float32(-np.inf)          # a masked entry keeps probability 0
+    print(f"one-pass rows: vocab {vocab} rows {len(row_of)} contexts {ctx}", flush=True)
+    got, err = gpu_lib.tree_softmax_rows(torch.from_numpy(lg).cuda(), torch.from_numpy(row_of).cuda(),
+                                         inv_temperature=0.8)
+    torch.cuda.synchronize()
+    assert int(err.item()) == oracle.probs.ERR_ROW
+    g = got.cpu().numpy()
+    want, werr = oracle.softmax_rows(lg, inv_temperature=0.8)  # one row per context
+    assert werr == 0
+    ok = (row_of >= 0) & (row_of < ctx)
+    assert np.all(g[~ok] == 0)
+    check(g[ok], want[row_of[ok]])
+    assert np.all(g[row_of == 1][:, 17] == 0)
+
+
 def test_softmax_rows_feed_acceptance(gpu_lib):
     """Rows produced on the GPU drive the acceptance exactly as the oracle's
     acceptance run on the same rows."""

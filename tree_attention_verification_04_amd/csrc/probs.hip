@@ -8,11 +8,16 @@
 // "端侧大模型推测解码草稿模型动态剪枝策略：详解基于重要性采样的树形验证并行加速机制"
 // (ufo.work/2026/525), §7.1, log-sum-exp trick).
 //
-// Two kernels, both HBM-bound: k_row_stats takes the (max, sum of exp) of each
+// With many output rows (enough workgroups to fill the GPU) and a row that fits on
+// one compute unit, one kernel (k_row_fused): a workgroup of 1024 threads reads a
+// context row once into registers and LDS, reduces it to (max, sum of exp), keeps
+// the exponentials, and writes the probability rows of the consecutive output rows
+// of its group that share that context (siblings in level order).  Otherwise two
+// kernels, both HBM-bound: k_row_stats takes the (max, sum of exp) of each
 // 8192-element chunk of each context row; k_row_write merges the chunk statistics
 // of a row and writes one chunk of probabilities for 8 consecutive output rows,
-// loading a context chunk once for a run of siblings.  Logits are read twice
-// (once per pass), probabilities written once.
+// loading a context chunk once for a run of siblings.  There, logits are read twice
+// (once per pass); probabilities are written once either way.
 //
 // tree_softmax_rows_kept: the same rows restricted to a kept set of tokens per
 // context row, zero elsewhere -- the distribution a pruned draft actually samples
@@ -21,6 +26,7 @@
 // minus infinity elsewhere, gives the same softmax because the constant cancels).
 // One workgroup per output row (k_row_keep).
 #include <algorithm>
+#include <mutex>
 
 #include "tv_common.h"
 
@@ -171,6 +177,156 @@ __global__ void __launch_bounds__(kRowThreads) k_row_write(RowArgs a) {
   }
 }
 
+// ---- one pass, the context row on chip
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kFusedLdsFloats = 40448;  // the part of a row past the registers (158 KB)
+constexpr int kFusedMinRows = 256;      // output rows for at least one workgroup per CU
+constexpr float kLog2E = 1.44269504088896340736f;
+
+template <int kR>
+constexpr int fused_min_vocab() { return kFusedThreads * kR; }
+template <int kR>
+constexpr int fused_max_vocab() { return kFusedThreads * kR + kFusedLdsFloats; }
+
+// the workgroup's maximum / sum of one value per thread (every thread gets it);
+// s_red holds one value per wavefront
+__device__ __forceinline__ float fused_max(float v, float* s_red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  __syncthreads();  // s_red free (its previous use has been read by every thread)
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kFusedWaves; ++w) m = fmaxf(m, s_red[w]);
+  return m;
+}
+__device__ __forceinline__ float fused_sum(float v, float* s_red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kFusedWaves; ++w) s += s_red[w];
+  return s;
+}
+
+// Workgroup g writes output rows g * group .. + group - 1.  Thread t holds the
+// float4s at 4 (t + 1024 j), j < kR / 4, of the current context row in registers,
+// and the row past 1024 kR in LDS (its own float4s at the same stride), first as
+// t * logits, then as exp(t * logits - max).  A bad context row index writes a zero
+// row and sets its error bit.  The vocabulary is a multiple of 4 in
+// [fused_min_vocab<kR>(), fused_max_vocab<kR>()] (the register part is always
+// whole, so its accesses need no bounds); rows are 16-byte aligned.
+template <int kR>
+__global__ void __launch_bounds__(kFusedThreads) k_row_fused(RowArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float s_tail[];
+  __shared__ float s_red[kFusedWaves];
+  static_assert(kR % 4 == 0, "whole float4s in registers");
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * a.group, i1 = min(a.rows, i0 + a.group);
+  constexpr int reg_end = kFusedThreads * kR;
+  float e[kR];
+  float inv = 0.0f;
+  int r_prev = -1;
+  for (int i = i0; i < i1; ++i) {
+    const int r = a.row_of != nullptr ? a.row_of[i] : i;
+    float* out = a.probs + static_cast<long>(i) * a.vocab;
+    if (r < 0 || r >= a.ctx_rows) {  // bad context row: zeros and the error bit
+      if (tid == 0) atomicOr(a.err, TV_ERR_ROW);
+      for (int k = 4 * tid; k < a.vocab; k += 4 * kFusedThreads)
+        __builtin_nontemporal_store(f32x4_t{0.0f, 0.0f, 0.0f, 0.0f},
+                                    reinterpret_cast<f32x4_t*>(out + k));
+      continue;
+    }
+    if (r != r_prev) {
+      const float* x = a.logits + static_cast<long>(r) * a.vocab;
+      // (a thread reads and writes only its own float4s of the LDS part, so a new
+      // row needs no barrier; s_red is guarded inside the reductions)
+      // the register part, then the LDS part by direct loads (lane l of a wavefront
+      // writes 16 bytes at the wavefront's base + 16 l, which is this thread's own
+      // float4): every load of the row in flight at once
+      const float4* xt = reinterpret_cast<const float4*>(x) + tid;
+#pragma unroll
+      for (int j = 0; j < kR / 4; ++j) {
+        const float4 v = xt[kFusedThreads * j];
+        e[4 * j] = v.x;
+        e[4 * j + 1] = v.y;
+        e[4 * j + 2] = v.z;
+        e[4 * j + 3] = v.w;
+      }
+      const int wave_base = 4 * (tid & ~63);
+      for (int k = reg_end + 4 * tid, j = 0; k < a.vocab; k += 4 * kFusedThreads, ++j)
+        __builtin_amdgcn_global_load_lds(
+            x + k,
+            (__attribute__((address_space(3))) void*)(s_tail + wave_base + 4 * kFusedThreads * j),
+            16, 0, 0);
+      // in log2 units: c x with c = t log2(e) (t > 0, so -inf stays -inf), then
+      // exp2 on the vector ALU; the argument's rounding is that of t x in expf(t x - m)
+      const float c = a.t * kLog2E;
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kR; ++q) {
+        e[q] = c * e[q];
+        m = fmaxf(m, e[q]);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the LDS part has landed
+      for (int k = reg_end + 4 * tid; k < a.vocab; k += 4 * kFusedThreads) {
+        float4 w = *reinterpret_cast<const float4*>(s_tail + (k - reg_end));
+        w.x = c * w.x;
+        w.y = c * w.y;
+        w.z = c * w.z;
+        w.w = c * w.w;
+        m = fmaxf(fmaxf(m, fmaxf(w.x, w.y)), fmaxf(w.z, w.w));
+        *reinterpret_cast<float4*>(s_tail + (k - reg_end)) = w;
+      }
+      m = fused_max(m, s_red);
+      // four running sums per thread (one per float4 lane), then the workgroup's
+      float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kR / 4; ++j) {
+        e[4 * j] = __builtin_amdgcn_exp2f(e[4 * j] - m);
+        e[4 * j + 1] = __builtin_amdgcn_exp2f(e[4 * j + 1] - m);
+        e[4 * j + 2] = __builtin_amdgcn_exp2f(e[4 * j + 2] - m);
+        e[4 * j + 3] = __builtin_amdgcn_exp2f(e[4 * j + 3] - m);
+        s0 += e[4 * j];
+        s1 += e[4 * j + 1];
+        s2 += e[4 * j + 2];
+        s3 += e[4 * j + 3];
+      }
+      for (int k = reg_end + 4 * tid; k < a.vocab; k += 4 * kFusedThreads) {
+        float4 w = *reinterpret_cast<const float4*>(s_tail + (k - reg_end));
+        w.x = __builtin_amdgcn_exp2f(w.x - m);
+        w.y = __builtin_amdgcn_exp2f(w.y - m);
+        w.z = __builtin_amdgcn_exp2f(w.z - m);
+        w.w = __builtin_amdgcn_exp2f(w.w - m);
+        s0 += w.x;
+        s1 += w.y;
+        s2 += w.z;
+        s3 += w.w;
+        *reinterpret_cast<float4*>(s_tail + (k - reg_end)) = w;
+      }
+      const float sum = fused_sum((s0 + s1) + (s2 + s3), s_red);
+      inv = 1.0f / sum;
+      r_prev = r;
+    }
+    // streaming stores: the rows are written once and not read here
+    f32x4_t* ot = reinterpret_cast<f32x4_t*>(out) + tid;
+#pragma unroll
+    for (int j = 0; j < kR / 4; ++j) {
+      const f32x4_t v = {e[4 * j] * inv, e[4 * j + 1] * inv, e[4 * j + 2] * inv,
+                         e[4 * j + 3] * inv};
+      __builtin_nontemporal_store(v, ot + kFusedThreads * j);
+    }
+    for (int k = reg_end + 4 * tid; k < a.vocab; k += 4 * kFusedThreads) {
+      const float4 w = *reinterpret_cast<const float4*>(s_tail + (k - reg_end));
+      const f32x4_t v = {w.x * inv, w.y * inv, w.z * inv, w.w * inv};
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(out + k));
+    }
+  }
+}
+
 constexpr int kKeepMax = kRowThreads;  // kept ids per context row: one per thread
 
 struct KeptArgs {
@@ -234,6 +390,25 @@ __global__ void __launch_bounds__(kRowThreads) k_row_keep(KeptArgs a) {
 
 }  // namespace
 
+// register floats per thread of the one-pass instances: 88 (vocabularies 90112 ..
+// 130560) and 112 (114688 .. 155136); four wavefronts per SIMD
+constexpr int kFusedR1 = 88;
+constexpr int kFusedR2 = 112;
+
+void set_fused_attributes() {
+  static std::mutex mu;
+  static uint32_t done = 0;  // one bit per device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 32) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done & (1u << dev)) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_row_fused<kFusedR1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsFloats * 4);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_row_fused<kFusedR2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLdsFloats * 4);
+  done |= 1u << dev;
+}
+
 }  // namespace tv
 
 extern "C" size_t tree_softmax_rows_workspace_size(int32_t ctx_rows, int32_t vocab) {
@@ -280,6 +455,26 @@ extern "C" int tree_softmax_rows(const float* logits, int32_t ctx_rows, int32_t 
   // float4 rows need every row to start 16-byte aligned
   const bool vec = vocab % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) % 16) == 0 &&
                    (reinterpret_cast<uintptr_t>(probs) % 16) == 0;
+  const bool fit1 = vocab >= tv::fused_min_vocab<tv::kFusedR1>() &&
+                    vocab <= tv::fused_max_vocab<tv::kFusedR1>();
+  const bool fit2 = vocab >= tv::fused_min_vocab<tv::kFusedR2>() &&
+                    vocab <= tv::fused_max_vocab<tv::kFusedR2>();
+  if (vec && rows >= tv::kFusedMinRows && (fit1 || fit2)) {
+    // one pass: groups of consecutive output rows, at least one workgroup per CU
+    tv::set_fused_attributes();
+    a.group = std::max(1, std::min(tv::kRowGroup, rows / tv::kFusedMinRows));
+    const int groups = tv::ceil_div(rows, a.group);
+    const bool small = fit1;
+    const int reg = (small ? tv::kFusedR1 : tv::kFusedR2) * tv::kFusedThreads;
+    const size_t lds = static_cast<size_t>(vocab - reg) * sizeof(float);
+    if (small)
+      hipLaunchKernelGGL(tv::k_row_fused<tv::kFusedR1>, dim3(groups), dim3(tv::kFusedThreads), lds,
+                         s, a);
+    else
+      hipLaunchKernelGGL(tv::k_row_fused<tv::kFusedR2>, dim3(groups), dim3(tv::kFusedThreads), lds,
+                         s, a);
+    return tv::check_launch("tree_softmax_rows/fused");
+  }
   if (vec)
     hipLaunchKernelGGL(tv::k_row_stats<true>, dim3(chunks, ctx_rows), dim3(tv::kRowThreads), 0, s, a);
   else
