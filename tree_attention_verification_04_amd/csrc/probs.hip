@@ -215,7 +215,8 @@ __device__ __forceinline__ float fused_sum(float v, float* s_red) {
 // Workgroup g writes output rows g * group .. + group - 1.  Thread t holds the
 // float4s at 4 (t + 1024 j), j < kR / 4, of the current context row in registers,
 // and the row past 1024 kR in LDS (its own float4s at the same stride), first as
-// t * logits, then as exp(t * logits - max).  A bad context row index writes a zero
+// c * logits with c = t log2(e), then as exp2(c * logits - max), which is
+// exp(t * logits - max / log2(e)).  A bad context row index writes a zero
 // row and sets its error bit.  The vocabulary is a multiple of 4 in
 // [fused_min_vocab<kR>(), fused_max_vocab<kR>()] (the register part is always
 // whole, so its accesses need no bounds); rows are 16-byte aligned.
