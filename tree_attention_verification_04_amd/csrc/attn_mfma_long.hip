@@ -399,7 +399,15 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     uint32_t o0, o1;  // byte offsets of this lane's two rows (before the chunk offset)
     uint32_t anc;     // this lane's byte offset of the tile's ancestor dword
   };
-  auto tile_src = [&](int it) __attribute__((always_inline)) -> Src {
+  // the physical block of tile it (clamped to the last tile) when it is a prefix
+  // tile, else 0: one scalar load, read ahead of its use by the loop below
+  auto tile_blk = [&](int it) __attribute__((always_inline)) -> int {
+    int kind, base;
+    tile_kind(min(it, n_tiles - 1), kind, base);
+    return kind == 0 ? bt_row[base / kKT] : 0;
+  };
+  // source of tile it given its block (tile_blk(it))
+  auto tile_src_b = [&](int it, int blk) __attribute__((always_inline)) -> Src {
     int kind, base;
     tile_kind(min(it, n_tiles - 1), kind, base);
     Src s;
@@ -407,7 +415,6 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     if (kind == 0) {
       s.anc = anc_lane;
       stride = kD * 2;
-      const int blk = bt_row[base / kKT];
       nvalid = min(kKT, plen - base);
       if (blk < 0 || blk >= a.num_blocks) {
         if (tid == 0) atomicOr(a.err, TV_ERR_BLOCK);
@@ -430,6 +437,9 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     s.o0 = min(lrow, nvalid - 1) * stride;
     s.o1 = min(32 + lrow, nvalid - 1) * stride;
     return s;
+  };
+  auto tile_src = [&](int it) __attribute__((always_inline)) -> Src {
+    return tile_src_b(it, tile_blk(it));
   };
   // the loads of one iteration: K and ancestor words of the tile of sk, V of sv
   auto issue_k = [&](const Src& sk, int slot_k) __attribute__((always_inline)) {
@@ -893,6 +903,11 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
     uint32_t px[8], py[8];   // probabilities of two halves
 #pragma unroll
     for (int v = 0; v < 8; ++v) px[v] = 0u;
+    // bf16 mode: the block of the tile whose loads the next iteration issues, read
+    // one iteration ahead, so that its scalar load has completed by the barrier
+    // between (a read at the top of the iteration stalled every iteration on it)
+    int blk_ahead = 0;
+    if constexpr (!kFp8 && !kMma8) blk_ahead = tile_blk(3);
 
     // tile iteration i (ring slot S = i % 4) = half-steps 2i and 2i+1
     auto body = [&](int i, auto slot) __attribute__((always_inline)) {
@@ -908,10 +923,12 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
       if constexpr (kMma8) convert_v((S + 1) % kRing);  // V(i + 1), landed last iteration
       Src sk{};
       Src8 sk8{};
-      if constexpr (kMma8)
+      if constexpr (kMma8) {
         sk8 = tile_src8(i + 3);
-      else if constexpr (!kFp8)
-        sk = tile_src(i + 3);
+      } else if constexpr (!kFp8) {
+        sk = tile_src_b(i + 3, blk_ahead);
+        blk_ahead = tile_blk(i + 4);
+      }
       // the K group of this iteration's loads, then the V group (see kIssueAt)
       const auto hk = [&]() __attribute__((always_inline)) {
         if constexpr (kMma8)
