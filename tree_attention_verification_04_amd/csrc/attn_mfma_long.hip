@@ -904,8 +904,8 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
 #pragma unroll
     for (int v = 0; v < 8; ++v) px[v] = 0u;
     // bf16 mode: the block of the tile whose loads the next iteration issues, read
-    // one iteration ahead, so that its scalar load has completed by the barrier
-    // between (a read at the top of the iteration stalled every iteration on it)
+    // at the end of this one, so that the barrier's wait covers its scalar load (a
+    // read at the top of the iteration stalled every iteration on it)
     int blk_ahead = 0;
     if constexpr (!kFp8 && !kMma8) blk_ahead = tile_blk(3);
 
@@ -927,7 +927,6 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         sk8 = tile_src8(i + 3);
       } else if constexpr (!kFp8) {
         sk = tile_src_b(i + 3, blk_ahead);
-        blk_ahead = tile_blk(i + 4);
       }
       // the K group of this iteration's loads, then the V group (see kIssueAt)
       const auto hk = [&]() __attribute__((always_inline)) {
@@ -954,7 +953,10 @@ __device__ __forceinline__ void long_item(const AttnArgs& a, const int xcd, cons
         // probabilities of tile i half 1, scores of tile i+1 half 0, P.V of tile i half 0
         half_step(s0, (S + 1) % kRing, 0, py, S, 0, s1, px, !full, w >> 16, hv);
       }
-      if constexpr (!kFp8 && !kMma8) sv = sk;
+      if constexpr (!kFp8 && !kMma8) {
+        sv = sk;
+        blk_ahead = tile_blk(i + 4);  // lands by the barrier's wait
+      }
       wait_iteration();
     };
 
