@@ -97,6 +97,17 @@ def test_softmax_rows_one_pass(gpu_lib, vocab, levels):
     assert np.all(g[row_of == 1][:, 17] == 0)
 
 
+def test_softmax_rows_one_pass_own_rows(gpu_lib):
+    """The one-pass kernel without row_of (output row i from context row i), groups
+    of one row, the smaller instance with an LDS part."""
+    lg = logits_rows(300, 100000, seed=12)
+    got, err = gpu_lib.tree_softmax_rows(torch.from_numpy(lg).cuda(), inv_temperature=1.2)
+    torch.cuda.synchronize()
+    want, werr = oracle.softmax_rows(lg, inv_temperature=1.2)
+    assert int(err.item()) == werr == 0
+    check(got.cpu().numpy(), want)
+
+
 def test_softmax_rows_feed_acceptance(gpu_lib):
     """Rows produced on the GPU drive the acceptance exactly as the oracle's
     acceptance run on the same rows."""
